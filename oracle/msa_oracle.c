@@ -1,0 +1,243 @@
+/*
+ * msa_oracle.c -- plain fp64 CPU reference of the MSA hot path.
+ * TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline leg of the bench).
+ * Definitions and sources are documented in msa_oracle.h.
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math; plain C99).
+ */
+#include "msa_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- bf16 --- */
+
+double orc_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+uint16_t orc_bf16_from_double(double x)
+{
+    /* bf16 = 1 sign, 8 exponent, 7 fraction bits: 8 significant bits for
+     * normal numbers, and a fixed spacing of 2^-133 below 2^-126.  Round to
+     * that grid with nearbyint (round-half-even in the default mode). */
+    if (isnan(x)) return 0x7FC0;
+    if (x == 0.0) return signbit(x) ? 0x8000 : 0x0000;
+    if (isinf(x)) return signbit(x) ? 0xFF80 : 0x7F80;
+    int e;
+    frexp(x, &e);                 /* |x| = m * 2^e, m in [0.5, 1) */
+    int q = e - 8;                /* spacing of an 8-bit significand */
+    if (q < -133) q = -133;       /* subnormal spacing */
+    double y = ldexp(nearbyint(ldexp(x, -q)), q);
+    if (fabs(y) > 3.3895313892515355e38) /* largest finite bf16 (0x7F7F) */
+        return signbit(x) ? 0xFF80 : 0x7F80;
+    float f = (float)y;           /* exact: y is on the bf16 grid */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------- document offset tables */
+
+void orc_group_ids(const int64_t* doc_ids, int64_t n, int64_t* group_ids)
+{
+    /* [P2 5.3]: mark where consecutive ids differ, running-sum the marks,
+     * start from 0, then add 1. */
+    int64_t g = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (i > 0 && doc_ids[i] != doc_ids[i - 1]) g += 1;
+        group_ids[i] = g + 1;
+    }
+}
+
+int64_t orc_doc_tok_offsets(const int64_t* doc_ids, int64_t n, int64_t* doc_tok_off)
+{
+    int64_t* gid = (int64_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+    orc_group_ids(doc_ids, n, gid);
+    int64_t n_groups = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (gid[i] != n_groups) {      /* first token of group gid[i] */
+            doc_tok_off[n_groups] = i;
+            n_groups = gid[i];
+        }
+    }
+    doc_tok_off[n_groups] = n;
+    free(gid);
+    return n_groups;
+}
+
+int64_t orc_block_offsets(const int64_t* doc_tok_off, int32_t n_docs,
+                          int64_t* doc_blk_off, int32_t* max_doc_blocks)
+{
+    int32_t mx = 0;
+    doc_blk_off[0] = 0;
+    for (int32_t d = 0; d < n_docs; ++d) {
+        int64_t len = doc_tok_off[d + 1] - doc_tok_off[d];
+        int64_t nb = (len + ORC_BLOCK - 1) / ORC_BLOCK;
+        doc_blk_off[d + 1] = doc_blk_off[d] + nb;
+        if (nb > mx) mx = (int32_t)nb;
+    }
+    if (max_doc_blocks) *max_doc_blocks = mx;
+    return doc_blk_off[n_docs];
+}
+
+/* ---------------------------------------------------------------- pooling */
+
+void orc_pool(int32_t n_layers, const uint16_t* x, int64_t n_tok,
+              const int64_t* doc_tok_off, const int64_t* doc_blk_off, int32_t n_docs,
+              int64_t n_blk, uint16_t* xbar)
+{
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const uint16_t* xl = x + (size_t)l * (size_t)n_tok * ORC_ROW;
+        uint16_t* ol = xbar + (size_t)l * (size_t)n_blk * ORC_ROW;
+        for (int32_t d = 0; d < n_docs; ++d) {
+            int64_t s = doc_tok_off[d], e = doc_tok_off[d + 1];
+            for (int64_t j = 0; doc_blk_off[d] + j < doc_blk_off[d + 1]; ++j) {
+                int64_t t0 = s + ORC_BLOCK * j;
+                int64_t t1 = t0 + ORC_BLOCK < e ? t0 + ORC_BLOCK : e;
+                uint16_t* out = ol + (size_t)(doc_blk_off[d] + j) * ORC_ROW;
+                for (int c = 0; c < ORC_ROW; ++c) {
+                    double sum = 0.0;
+                    for (int64_t t = t0; t < t1; ++t)
+                        sum += orc_bf16_to_double(xl[(size_t)t * ORC_ROW + c]);
+                    out[c] = orc_bf16_from_double(sum / (double)(t1 - t0));
+                }
+            }
+        }
+    }
+}
+
+void orc_head_norms(const uint16_t* rows, int64_t n_rows, double* norms)
+{
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int h = 0; h < ORC_H; ++h) {
+            double ss = 0.0;
+            for (int i = 0; i < ORC_D; ++i) {
+                double v = orc_bf16_to_double(rows[(size_t)r * ORC_ROW + h * ORC_D + i]);
+                ss += v * v;
+            }
+            norms[r * ORC_H + h] = sqrt(ss);
+        }
+}
+
+/* ---------------------------------------------------------------- routing */
+
+static double cosine(const uint16_t* a, const uint16_t* b)
+{
+    double ab = 0.0, aa = 0.0, bb = 0.0;
+    for (int i = 0; i < ORC_D; ++i) {
+        double x = orc_bf16_to_double(a[i]), y = orc_bf16_to_double(b[i]);
+        ab += x * y;
+        aa += x * x;
+        bb += y * y;
+    }
+    double na = sqrt(aa), nb = sqrt(bb);
+    if (na < 1e-8) na = 1e-8;
+    if (nb < 1e-8) nb = 1e-8;
+    return ab / (na * nb);
+}
+
+double orc_block_score(const uint16_t* q_row, const uint16_t* k_row)
+{
+    double s = 0.0;
+    for (int h = 0; h < ORC_H; ++h) s += cosine(q_row + h * ORC_D, k_row + h * ORC_D);
+    return s / ORC_H;
+}
+
+void orc_doc_scores(int32_t T, const uint16_t* qr, const uint16_t* krbar,
+                    const int64_t* doc_blk_off, int32_t n_docs, double* S)
+{
+    for (int32_t d = 0; d < n_docs; ++d) {
+        double best = -INFINITY;
+        for (int64_t b = doc_blk_off[d]; b < doc_blk_off[d + 1]; ++b)
+            for (int32_t t = 0; t < T; ++t) {
+                double s = orc_block_score(qr + (size_t)t * ORC_ROW, krbar + (size_t)b * ORC_ROW);
+                if (s > best) best = s;
+            }
+        S[d] = best;
+    }
+}
+
+/* ------------------------------------------------------------------ top-k */
+
+typedef struct { double s; int32_t id; } scored;
+
+static int by_score_desc_id_asc(const void* pa, const void* pb)
+{
+    const scored* a = (const scored*)pa;
+    const scored* b = (const scored*)pb;
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+    return (a->id > b->id) - (a->id < b->id);
+}
+
+void orc_topk(const double* S, int32_t n_docs, int32_t k, int32_t* ids, double* scores)
+{
+    scored* all = (scored*)malloc((size_t)(n_docs > 0 ? n_docs : 1) * sizeof(scored));
+    for (int32_t d = 0; d < n_docs; ++d) { all[d].s = S[d]; all[d].id = d; }
+    qsort(all, (size_t)n_docs, sizeof(scored), by_score_desc_id_asc);
+    for (int32_t j = 0; j < k; ++j) { ids[j] = all[j].id; scores[j] = all[j].s; }
+    free(all);
+}
+
+/* ----------------------------------------------------------------- gather */
+
+int64_t orc_gather(const int32_t* ids, int32_t k, const int64_t* doc_blk_off,
+                   const uint16_t* kbar, const uint16_t* vbar,
+                   uint16_t* ctx_k, uint16_t* ctx_v)
+{
+    int64_t r = 0;
+    for (int32_t j = 0; j < k; ++j) {
+        int32_t d = ids[j];
+        for (int64_t b = doc_blk_off[d]; b < doc_blk_off[d + 1]; ++b, ++r) {
+            memcpy(ctx_k + (size_t)r * ORC_ROW, kbar + (size_t)b * ORC_ROW, ORC_ROW * sizeof(uint16_t));
+            memcpy(ctx_v + (size_t)r * ORC_ROW, vbar + (size_t)b * ORC_ROW, ORC_ROW * sizeof(uint16_t));
+        }
+    }
+    return r;
+}
+
+/* ----------------------------------------------------------------- decode */
+
+void orc_decode(int32_t Hq, const uint16_t* q,
+                const uint16_t* ctx_k, const uint16_t* ctx_v, int64_t n_ctx,
+                const uint16_t* loc_k, const uint16_t* loc_v, int64_t n_loc,
+                double scale, double* out)
+{
+    int32_t group = Hq / ORC_H;
+    int64_t n = n_ctx + n_loc;
+    double* s = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    for (int32_t hq = 0; hq < Hq; ++hq) {
+        int32_t g = hq / group;
+        const uint16_t* qh = q + (size_t)hq * ORC_D;
+        double* o = out + (size_t)hq * ORC_D;
+        for (int i = 0; i < ORC_D; ++i) o[i] = 0.0;
+        if (n == 0) continue;
+        /* pass 1: scores and their maximum */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < n; ++j) {
+            const uint16_t* kr = j < n_ctx ? ctx_k + (size_t)j * ORC_ROW
+                                           : loc_k + (size_t)(j - n_ctx) * ORC_ROW;
+            double dot = 0.0;
+            for (int i = 0; i < ORC_D; ++i)
+                dot += orc_bf16_to_double(qh[i]) * orc_bf16_to_double(kr[g * ORC_D + i]);
+            s[j] = scale * dot;
+            if (s[j] > m) m = s[j];
+        }
+        /* pass 2: normaliser and weighted values */
+        double z = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            const uint16_t* vr = j < n_ctx ? ctx_v + (size_t)j * ORC_ROW
+                                           : loc_v + (size_t)(j - n_ctx) * ORC_ROW;
+            double w = exp(s[j] - m);
+            z += w;
+            for (int i = 0; i < ORC_D; ++i) o[i] += w * orc_bf16_to_double(vr[g * ORC_D + i]);
+        }
+        for (int i = 0; i < ORC_D; ++i) o[i] /= z;
+    }
+    free(s);
+}

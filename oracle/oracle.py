@@ -1,0 +1,222 @@
+"""ctypes binding of the fp64 C oracle (msa_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  All arrays are numpy; bf16 travels as uint16.
+Row layout: [row][8 heads][128 dims].  Definitions and citations are in
+msa_oracle.h; this module only marshals arguments and loops over
+(layer, query) pairs where the C functions work on one pair.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "msa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+H, D, BLOCK = 8, 128, 64
+ROW = H * D
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C99, fp64, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_to_double.restype = f64
+        L.orc_bf16_from_double.argtypes = [f64]
+        L.orc_bf16_from_double.restype = ctypes.c_uint16
+        L.orc_group_ids.argtypes = [P, i64, P]
+        L.orc_doc_tok_offsets.argtypes = [P, i64, P]
+        L.orc_doc_tok_offsets.restype = i64
+        L.orc_block_offsets.argtypes = [P, i32, P, P]
+        L.orc_block_offsets.restype = i64
+        L.orc_pool.argtypes = [i32, P, i64, P, P, i32, i64, P]
+        L.orc_head_norms.argtypes = [P, i64, P]
+        L.orc_block_score.argtypes = [P, P]
+        L.orc_block_score.restype = f64
+        L.orc_doc_scores.argtypes = [i32, P, P, P, i32, P]
+        L.orc_topk.argtypes = [P, i32, i32, P, P]
+        L.orc_gather.argtypes = [P, i32, P, P, P, P, P]
+        L.orc_gather.restype = i64
+        L.orc_decode.argtypes = [i32, P, P, P, i64, P, P, i64, f64, P]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+def _i64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int64)
+
+
+# ------------------------------------------------------------------ bf16 ---
+
+def bf16_to_f64(a) -> np.ndarray:
+    """Exact values of bf16 bit patterns (vectorised through the C routine's rule)."""
+    a = np.asarray(a, dtype=np.uint16)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_from_f64_scalar(x: float) -> int:
+    return int(lib().orc_bf16_from_double(float(x)))
+
+
+def bf16_from_f64(x) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float64)
+    f = lib().orc_bf16_from_double
+    out = np.fromiter((f(float(v)) for v in x.ravel()), dtype=np.uint16, count=x.size)
+    return out.reshape(x.shape)
+
+
+# --------------------------------------------------------- offset tables ---
+
+def group_ids(doc_ids) -> np.ndarray:
+    a = _i64(doc_ids)
+    out = np.empty_like(a)
+    lib().orc_group_ids(_p(a), a.size, _p(out))
+    return out
+
+
+def doc_tok_offsets(doc_ids) -> np.ndarray:
+    a = _i64(doc_ids)
+    out = np.empty(a.size + 1, np.int64)
+    n = lib().orc_doc_tok_offsets(_p(a), a.size, _p(out))
+    return out[: n + 1].copy()
+
+
+def block_offsets(doc_tok_off):
+    t = _i64(doc_tok_off)
+    n_docs = t.size - 1
+    out = np.empty(n_docs + 1, np.int64)
+    mx = ctypes.c_int32(0)
+    n_blk = lib().orc_block_offsets(_p(t), n_docs, _p(out), ctypes.byref(mx))
+    return out, int(n_blk), int(mx.value)
+
+
+# -------------------------------------------------------------- pooling ---
+
+def pool(x, doc_tok_off, doc_blk_off) -> np.ndarray:
+    """x: [L][N_tok][8][128] uint16 -> [L][N_blk][8][128] uint16."""
+    x = _u16(x)
+    L, n_tok = x.shape[0], x.shape[1]
+    t, b = _i64(doc_tok_off), _i64(doc_blk_off)
+    n_docs, n_blk = t.size - 1, int(b[-1])
+    out = np.zeros((L, n_blk, H, D), np.uint16)
+    lib().orc_pool(L, _p(x), n_tok, _p(t), _p(b), n_docs, n_blk, _p(out))
+    return out
+
+
+def head_norms(rows) -> np.ndarray:
+    """rows: [..., 8, 128] uint16 -> [..., 8] float64."""
+    rows = _u16(rows)
+    n = rows.size // ROW
+    out = np.empty(n * H, np.float64)
+    lib().orc_head_norms(_p(rows), n, _p(out))
+    return out.reshape(rows.shape[:-1])
+
+
+# -------------------------------------------------------------- routing ---
+
+def block_score(q_row, k_row) -> float:
+    q, k = _u16(q_row), _u16(k_row)
+    assert q.size == ROW and k.size == ROW
+    return float(lib().orc_block_score(_p(q), _p(k)))
+
+
+def doc_scores(qr, krbar, doc_blk_off) -> np.ndarray:
+    """qr: [T][8][128]; krbar: [n_blk][8][128] -> S[n_docs] (float64, -inf if empty)."""
+    q, k, b = _u16(qr), _u16(krbar), _i64(doc_blk_off)
+    T, n_docs = q.shape[0], b.size - 1
+    S = np.empty(n_docs, np.float64)
+    lib().orc_doc_scores(T, _p(q), _p(k), _p(b), n_docs, _p(S))
+    return S
+
+
+def doc_scores_all(qr, krbar, doc_blk_off) -> np.ndarray:
+    """qr: [L][B][T][8][128]; krbar: [L][n_blk][8][128] -> S[L][B][n_docs]."""
+    L, B = qr.shape[0], qr.shape[1]
+    n_docs = len(doc_blk_off) - 1
+    S = np.empty((L, B, n_docs), np.float64)
+    for l in range(L):
+        for b in range(B):
+            S[l, b] = doc_scores(qr[l, b], krbar[l], doc_blk_off)
+    return S
+
+
+def topk(S, k: int):
+    s = np.ascontiguousarray(S, dtype=np.float64)
+    ids = np.empty(k, np.int32)
+    sc = np.empty(k, np.float64)
+    lib().orc_topk(_p(s), s.size, k, _p(ids), _p(sc))
+    return ids, sc
+
+
+# --------------------------------------------------------------- gather ---
+
+def gather(ids, doc_blk_off, kbar, vbar):
+    """One (layer, query): kbar/vbar [n_blk][8][128] -> (ctx_k, ctx_v) [rows][8][128]."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    b = _i64(doc_blk_off)
+    kb, vb = _u16(kbar), _u16(vbar)
+    total = int(sum(b[i + 1] - b[i] for i in ids))
+    ck = np.zeros((max(total, 1), H, D), np.uint16)
+    cv = np.zeros((max(total, 1), H, D), np.uint16)
+    n = lib().orc_gather(_p(ids), ids.size, _p(b), _p(kb), _p(vb), _p(ck), _p(cv))
+    assert n == total
+    return ck[:total], cv[:total]
+
+
+# --------------------------------------------------------------- decode ---
+
+def decode(q, ctx_k, ctx_v, loc_k, loc_v, scale: float) -> np.ndarray:
+    """One (layer, query): q [Hq][128]; rows [n][8][128] -> out [Hq][128] float64."""
+    q = _u16(q)
+    Hq = q.shape[0]
+
+    def rows(a):
+        a = _u16(a) if a is not None and len(a) else np.zeros((1, H, D), np.uint16)
+        return a
+
+    ck, cv = _u16(ctx_k), _u16(ctx_v)
+    lk, lv = _u16(loc_k), _u16(loc_v)
+    n_ctx, n_loc = ck.shape[0], lk.shape[0]
+    ck_, cv_ = (ck, cv) if n_ctx else (rows(None), rows(None))
+    lk_, lv_ = (lk, lv) if n_loc else (rows(None), rows(None))
+    out = np.empty((Hq, D), np.float64)
+    lib().orc_decode(Hq, _p(q), _p(ck_), _p(cv_), n_ctx, _p(lk_), _p(lv_), n_loc, float(scale), _p(out))
+    return out
+
+
+__all__ = ["build", "lib", "bf16_to_f64", "bf16_from_f64", "bf16_from_f64_scalar", "group_ids",
+           "doc_tok_offsets", "block_offsets", "pool", "head_norms", "block_score", "doc_scores",
+           "doc_scores_all", "topk", "gather", "decode", "H", "D", "BLOCK", "ROW"]
