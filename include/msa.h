@@ -1,0 +1,234 @@
+/*
+ * msa.h -- C ABI of libmsa, the Memory Sparse Attention (MSA) hot path on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are web pages about MSA, cited by title and section):
+ *  [P1] yunpan.plus, "MSA端到端可训练记忆模型完整开源，支持亿级Token上下文", 整体设计 -> 架构
+ *       and 推理流水线: document K, V and routing key Kr are compressed by block mean
+ *       pooling; a routing projection Qr is compared with every pooled routing key by
+ *       cosine similarity, averaged over heads and maxed over tokens; the Top-k
+ *       documents' compressed K/V are concatenated with the query's local K/V for
+ *       autoregressive decoding.
+ *  [P2] xuqi2024.github.io, "【MSA】突破100M Token 上下文：记忆稀疏注意力架构深度解析",
+ *       3.3.2 (64-token blocks, Top-16), 5.2 (concatenation, varlen attention),
+ *       5.3 (map_tensor_to_group_ids).
+ *  [P5] xiaohongrsx.github.io, "MSA paper reading", 方法拆解 (8 KV heads x 128 dims,
+ *       18 routed layers, fixed 64-token blocks per document, Top-16 by cosine) and
+ *       推理全流程 (context = [Top-16 compressed KV ; local KV]; memory KV is fixed
+ *       while the local KV grows token by token).
+ *
+ * Conventions for every entry point:
+ *  - Shapes are fixed at H = 8 KV heads, D = 128, 64-token blocks.  bf16 values
+ *    travel as uint16_t bit patterns.  Layouts are layer-major and row-major; a
+ *    "row" is [8 heads][128 dims] = 1024 bf16.
+ *  - Pointers without a _host suffix are DEVICE pointers owned by the caller; the
+ *    library never allocates, frees or keeps them.  Workspaces are caller-owned
+ *    device memory of at least the size the matching *_workspace_size returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls
+ *    validate on the host, enqueue kernels on `stream` and return; results are
+ *    valid once the stream has been synchronised.  No call synchronises.
+ *  - Return value: MSA_OK, or an MSA_ERR_* code; host-checkable errors are
+ *    reported before anything is enqueued.  msa_last_error() gives a message for
+ *    the last failing call on the calling thread.  The library never aborts or
+ *    prints.  Device-side inconsistencies (offsets out of range, invalid ids) are
+ *    clamped, never read or written out of bounds.
+ *  - Calls on different streams that share an output or workspace race.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+#define MSA_HEADS 8          /* KV heads per routed layer                        [P5 方法拆解] */
+#define MSA_HEAD_DIM 128     /* head dimension                                   [P5 方法拆解] */
+#define MSA_BLOCK_TOKENS 64  /* pooling_kernel_size: tokens per compressed block [P2 3.3.2] */
+#define MSA_TILE_BLOCKS 16   /* blocks per tile of the route-key layout (below) */
+#define MSA_MAX_TOPK 256     /* largest k accepted by the top-k entry points */
+
+enum {
+    MSA_OK = 0,
+    MSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    MSA_ERR_SHAPE = 2,       /* a size is negative/zero where it must be positive, or inconsistent */
+    MSA_ERR_UNSUPPORTED = 3, /* a valid request outside what this build implements */
+    MSA_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_size figure */
+    MSA_ERR_HIP = 5          /* the HIP runtime reported an error while enqueueing */
+};
+
+int msa_abi_version(void);
+/* Static, never-NULL description of a status code. */
+const char* msa_status_string(int status);
+/* Message of the last non-OK return on the calling thread ("" if none). */
+const char* msa_last_error(void);
+
+/* ------------------------------------------------------------------ host helpers */
+
+/* [P2 5.3] Document offsets from per-token document ids.  A new document starts
+ * wherever consecutive ids differ (the ids need not be sorted or distinct).
+ * doc_ids_host[n_tok]; doc_tok_off_host must hold n_tok + 1 entries; on return
+ * doc_tok_off_host[0..*n_docs_host] are the first token of each document followed
+ * by n_tok.  Host memory only. */
+int msa_group_offsets_host(const int64_t* doc_ids_host, int64_t n_tok,
+                           int64_t* doc_tok_off_host, int32_t* n_docs_host);
+
+/* [P1 架构; P5 方法拆解] Block offsets of documents split into 64-token blocks,
+ * each document on its own grid (blocks never span documents; a final partial
+ * block still counts): doc_blk_off[d+1] - doc_blk_off[d] = ceil(len_d / 64).
+ * doc_tok_off_host[n_docs + 1] must be non-decreasing from 0.  Writes
+ * doc_blk_off_host[n_docs + 1], the total block count and the largest per-doc
+ * count.  Host memory only. */
+int msa_block_offsets_host(const int64_t* doc_tok_off_host, int32_t n_docs,
+                           int64_t* doc_blk_off_host, int64_t* n_blk_host,
+                           int32_t* max_doc_blocks_host);
+
+/* -------------------------------------------------------------- route-key layout
+ *
+ * Pooled routing keys are stored for the routing scan, not row-major.  Blocks are
+ * grouped in tiles of 16 (the last tile padded with zero rows); within a tile the
+ * 16 blocks' 8-dim chunks are interleaved:
+ *
+ *   krbar_route[l][tile][h][c][b][e]  = Kr-bar of block (tile*16 + b), head h,
+ *                                       dims c*8 + e          (c < 16, b < 16, e < 8)
+ *   krbar_norm [l][tile][h][b]        = || Kr-bar[tile*16 + b][h] ||_2 (fp32; 0 for padding)
+ *
+ * so each 1 KiB of a tile is one matrix-core operand fragment for 16 blocks.
+ * Sizes per layer: msa_route_tiles(n_blk) * 16384 bf16 and * 128 floats. */
+int64_t msa_route_tiles(int64_t n_blk);
+
+/* ------------------------------------------------------------- A1: block pooling
+ *
+ * [P1 架构, 推理流水线 stage 1; P2 3.3.2; P5 方法拆解] For every layer l, document d
+ * (tokens [doc_tok_off[d], doc_tok_off[d+1])) and block j of d, the block covers
+ * tokens [s_d + 64 j, min(s_d + 64 j + 64, e_d)) and its value is the mean over
+ * those real tokens (a final partial block is averaged over its own tokens),
+ * accumulated in fp32 and rounded to bf16 (nearest-even).  Applied to K, V and Kr.
+ *
+ *   k, v, kr       [n_layers][n_tok][8][128] bf16, per-token inputs
+ *   doc_tok_off    [n_docs + 1] int64, device
+ *   doc_blk_off    [n_docs + 1] int64, device (as msa_block_offsets_host computes)
+ *   kbar, vbar     [n_layers][n_blk][8][128] bf16, row-major outputs
+ *   krbar_route    route-key layout (above), output; krbar_norm its norms, output
+ *
+ * Norms are of the rounded bf16 Kr-bar.  Errors: NULL pointers, n_layers/n_docs < 1,
+ * n_tok < 0, n_blk < 0. */
+int msa_pool_blocks(int32_t n_layers, const uint16_t* k, const uint16_t* v, const uint16_t* kr,
+                    int64_t n_tok, const int64_t* doc_tok_off, const int64_t* doc_blk_off,
+                    int32_t n_docs, int64_t n_blk,
+                    uint16_t* kbar, uint16_t* vbar, uint16_t* krbar_route, float* krbar_norm,
+                    void* stream);
+
+/* Routing keys that already exist row-major ([n_layers][n_blk][8][128] bf16, e.g. a
+ * memory bank built elsewhere) -> route-key layout + norms, as msa_pool_blocks
+ * writes them.  Errors: NULL pointers, n_layers < 1, n_blk < 0. */
+int msa_pack_route_keys(int32_t n_layers, const uint16_t* krbar_rows, int64_t n_blk,
+                        uint16_t* krbar_route, float* krbar_norm, void* stream);
+
+/* --------------------------------------------------------------- A2: routing scan
+ *
+ * [P1 架构; P2 3.3.3, 5.2; P5 方法拆解] For each layer l, query b, query token t and
+ * block n:  s(t, n) = (1/8) sum_h <Qr[t,h], Kr-bar[n,h]> / (max(|Qr[t,h]|, 1e-8) *
+ * max(|Kr-bar[n,h]|, 1e-8)); the document score is the max of s over t < T and the
+ * document's blocks:
+ *
+ *   doc_scores[l][b][d] = max_{t < T, n in d} s(t, n)      (-inf for a 0-block doc)
+ *
+ *   qr           [n_layers][B][T][8][128] bf16
+ *   krbar_route, krbar_norm   route-key layout of n_blk blocks per layer
+ *   doc_blk_off  [n_docs + 1] int64, device
+ *   doc_scores   [n_layers][B][n_docs] fp32, output (accumulate = 0) or in/out
+ *                (accumulate = 1: the result is max(previous value, new scores),
+ *                i.e. the scores of the query rows seen so far plus these T rows;
+ *                this is how a query grown by appended rows is re-routed exactly)
+ *   workspace    >= msa_route_scores_workspace_size(n_blk) bytes
+ *
+ * Queries with T >= 16 use bf16 matrix cores (fp32 accumulate); shorter ones use
+ * vector dot products.  Errors: NULL pointers, n_layers/B/T/n_docs < 1, n_blk < 0,
+ * small workspace. */
+size_t msa_route_scores_workspace_size(int64_t n_blk);
+int msa_route_scores(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
+                     const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
+                     const int64_t* doc_blk_off, int32_t n_docs, int32_t accumulate,
+                     float* doc_scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- A3: top-k docs
+ *
+ * [P1 架构; P2 3.3.2 (doc_top_k = 16), 5.2; P5 方法拆解] For each (layer, query): the
+ * k documents with the largest score, ordered by (score descending, id ascending).
+ *
+ *   doc_scores   [n_layers][B][n_docs] fp32 (NaN is not supported)
+ *   topk_ids     [n_layers][B][k] int32, output
+ *   topk_scores  [n_layers][B][k] fp32, output (may be NULL)
+ *
+ * Errors: NULL pointers, k < 1, k > n_docs (MSA_ERR_SHAPE), k > MSA_MAX_TOPK
+ * (MSA_ERR_UNSUPPORTED), small workspace. */
+size_t msa_topk_docs_workspace_size(int32_t n_layers, int32_t B, int32_t n_docs, int32_t k);
+int msa_topk_docs(int32_t n_layers, int32_t B, const float* doc_scores, int32_t n_docs, int32_t k,
+                  int32_t* topk_ids, float* topk_scores,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* A2 then A3 with the document scores kept in the workspace (doc_scores may be
+ * NULL; if given it receives a copy of them). */
+size_t msa_route_topk_workspace_size(int32_t n_layers, int32_t B, int32_t n_docs, int64_t n_blk,
+                                     int32_t k);
+int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
+                   const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
+                   const int64_t* doc_blk_off, int32_t n_docs, int32_t k,
+                   int32_t* topk_ids, float* topk_scores, float* doc_scores,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------ A4: context gather
+ *
+ * [P1 架构 (selected compressed K/V concatenated with the local K/V); P2 5.2;
+ * P5 推理全流程] For each (layer, query): all blocks of the selected documents,
+ * documents in top-k order, blocks ascending, copied bit-exactly into a contiguous
+ * memory context.
+ *
+ *   topk_ids     [n_layers][B][k] int32 (ids outside [0, n_docs) contribute no rows)
+ *   doc_blk_off  [n_docs + 1] int64, device
+ *   kbar, vbar   [n_layers][n_blk][8][128] bf16
+ *   ctx_k, ctx_v [n_layers][B][max_ctx][8][128] bf16, output (rows >= ctx_len untouched)
+ *   ctx_len      [n_layers][B] int32, output
+ *
+ * max_doc_blocks is the caller's bound on blocks per document (from
+ * msa_block_offsets_host); max_ctx < k * max_doc_blocks is MSA_ERR_SHAPE.  Rows that
+ * would pass max_ctx (only if the bound was wrong) are dropped. */
+int msa_gather_ctx(int32_t n_layers, int32_t B, const int32_t* topk_ids, int32_t k,
+                   const int64_t* doc_blk_off, int32_t n_docs, int32_t max_doc_blocks,
+                   const uint16_t* kbar, const uint16_t* vbar, int64_t n_blk,
+                   int32_t max_ctx, uint16_t* ctx_k, uint16_t* ctx_v, int32_t* ctx_len,
+                   void* stream);
+
+/* -------------------------------------------------------------- A5: sparse decode
+ *
+ * [P1 架构; P2 5.2 (attention over the concatenated K/V); P5 推理全流程] One decode
+ * token of grouped-query attention per (layer, query): query head hq reads KV head
+ * hq / (Hq / 8); its output is sum_j softmax_j(scale * <q_hq, k_j>) v_j over the rows
+ * [memory context rows 0..ctx_len) ; [local rows 0..loc_len), with no mask.  Split
+ * over rows, online softmax in fp32, then merged.
+ *
+ *   q            [n_layers][B][Hq][128] bf16, Hq a multiple of 8, Hq <= 64
+ *   ctx_k, ctx_v [n_layers][B][max_ctx][8][128] bf16;  ctx_len [n_layers][B] int32
+ *   loc_k, loc_v [n_layers][B][max_loc][8][128] bf16;  loc_len [n_layers][B] int32
+ *   out          [n_layers][B][Hq][128] fp32 (zero where a query has no rows)
+ *
+ * Lengths are clamped to [0, max_ctx] / [0, max_loc].  loc_k/loc_v/loc_len may be
+ * NULL when max_loc == 0.  Errors: NULL pointers, sizes < 1, Hq % 8 != 0 (SHAPE),
+ * Hq > 64 (UNSUPPORTED), small workspace. */
+size_t msa_sparse_decode_workspace_size(int32_t n_layers, int32_t B, int32_t Hq, int32_t max_ctx,
+                                        int32_t max_loc);
+int msa_sparse_decode(int32_t n_layers, int32_t B, int32_t Hq, const uint16_t* q,
+                      const uint16_t* ctx_k, const uint16_t* ctx_v, const int32_t* ctx_len,
+                      int32_t max_ctx,
+                      const uint16_t* loc_k, const uint16_t* loc_v, const int32_t* loc_len,
+                      int32_t max_loc, float scale, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H */

@@ -1,0 +1,104 @@
+// msa_device.hpp -- device-side helpers shared by the libmsa kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kHeads = 8;
+constexpr int kDim = 128;
+constexpr int kRow = kHeads * kDim;        // 1024 bf16 per block/token row
+constexpr int kBlockTokens = 64;
+constexpr int kTile = 16;                  // blocks per route-key tile
+constexpr int kTileElems = kTile * kRow;   // 16384 bf16 = 32 KiB
+constexpr float kNormEps = 1e-8f;
+constexpr int kMaxTopk = 256;           // MSA_MAX_TOPK
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0x007FFFFFu) ? 0x40u : 0u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Order-preserving map fp32 -> uint32 (larger float <=> larger code).  Code 0 is
+// below every float's code and stands for "no score yet" (-inf on decode).
+__device__ __forceinline__ uint32_t ordered_code(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered_code(uint32_t c) {
+  if (c == 0u) return -__builtin_huge_valf();
+  uint32_t u = (c & 0x80000000u) ? (c & 0x7FFFFFFFu) : ~c;
+  return __uint_as_float(u);
+}
+
+// Max over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane gets it.
+__device__ __forceinline__ float row16_max(float v) {
+  int x = __float_as_int(v);
+  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false)));
+  x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false)));
+  x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false)));
+  x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
+// Sum over the 16 lanes of a DPP row; every lane gets it.
+__device__ __forceinline__ float row16_sum(float v) {
+  int x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Per-document max of block scores held one per lane in lanes [0, n) of a wave
+// (lanes >= n pass doc = -1).  Blocks of a document are contiguous, so a
+// segmented suffix max inside each run leaves the run's max in its first lane,
+// which folds it into the document score with one atomic max on its code.
+__device__ __forceinline__ void flush_doc_max(float v, int32_t doc, int n, uint32_t* __restrict__ codes) {
+  const int lane = __lane_id();
+  if (lane >= n) doc = -1;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float vo = __shfl_down(v, off, 64);
+    int32_t dn = __shfl_down(doc, off, 64);
+    if (lane + off < 64 && dn == doc) v = fmaxf(v, vo);
+  }
+  int32_t dprev = __shfl_up(doc, 1, 64);
+  bool head = (lane == 0) || (dprev != doc);
+  if (head && doc >= 0) atomicMax(codes + doc, ordered_code(v));
+}
+
+}  // namespace msa
