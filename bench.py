@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA hot path on one MI355X.
+
+Default workload: the 100M-token memory (18 routed layers x 1,562,500 pooled
+blocks x 8 heads x 128 dims, 100,000 documents, K-bar/V-bar and routing keys all
+HBM-resident), one 64-token query, Top-16 per layer, then gather and a GQA
+32/8 decode token over [memory context ; 4,096 local rows].
+
+One step = one pass of the whole path over that input: routing scan (all 18
+layers, one launch) -> top-k -> context gather -> sparse decode.  Memories that
+arrive per token (--workload tiny / 1m) also pool inside the step.  Inputs are
+generated on the GPU before timing.  Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routing scan GB/s (% HBM peak) + ms/query, 18 layers, 100M-token memory"
+HBM_PEAK_GBPS = 8000.0
+SCAN_BYTES_PER_BLOCK_LAYER = 2048 + 32    # bf16 Kr-bar row (8 x 128) + 8 fp32 norms
+DECODE_BYTES_PER_ROW = 2 * 8 * 128 * 2    # K and V row of all 8 KV heads
+POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="100m", choices=["tiny", "1m", "10m", "100m"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the hot path runs on a single MI355X here; "
+              "sharding over several GPUs is a design note, not built (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from routed_kv_memory_amd import msa
+    from synth import synth as S
+    from synth.device import DeviceInputs
+
+    msa.lib()
+    torch.cuda.set_device(int(os.environ.get("LOCAL_RANK", "0")))
+    dev = "cuda"
+    cfg = S.CONFIGS[args.workload]
+    L, B, T, k, Hq = cfg.n_layers, cfg.B, cfg.T, cfg.k, cfg.Hq
+    t_setup = time.time()
+    di = DeviceInputs(cfg, dev)
+
+    # ---------------------------------------------------------------- memory (outside timing)
+    pool_args = None
+    if cfg.per_token:
+        tok, kt_, vt_, krt_ = di.per_token()
+        blk, n_blk, max_db = msa.msa_block_offsets_host(tok)
+        tok_d = tok.to(dev)
+        n_tok = int(tok[-1])
+    else:
+        blk = di.prepooled_offsets()
+        n_blk = int(blk[-1])
+        max_db = int((blk[1:] - blk[:-1]).max())
+    n_docs = blk.numel() - 1
+    blk_d = blk.to(dev)
+    tiles = msa.msa_route_tiles(n_blk)
+    krt = torch.empty((L, tiles * 16, 8, 128), dtype=torch.bfloat16, device=dev)
+    krn = torch.empty((L, tiles * 16, 8), dtype=torch.float32, device=dev)
+    if cfg.per_token:
+        kbar = torch.empty((L, n_blk, 8, 128), dtype=torch.bfloat16, device=dev)
+        vbar = torch.empty_like(kbar)
+        pool_args = (kt_, vt_, krt_, tok_d, blk_d, n_blk, kbar, vbar, krt, krn)
+    else:
+        kbar, vbar = di.prepooled_content()
+        for l, rows in di.prepooled_route_rows():
+            msa.msa_pack_route_keys(rows.view(1, n_blk, 8, 128), n_blk, krt[l:l + 1], krn[l:l + 1])
+    blk_doc = torch.empty(tiles * 16, dtype=torch.int32, device=dev)
+    msa.msa_block_doc_map(blk_d, n_blk, blk_doc)
+    qr = di.qr()
+    q, lk, lv, ll = di.decode_inputs()
+    max_ctx = k * max_db
+    dsc = torch.empty((L, B, n_docs), dtype=torch.float32, device=dev)
+    ids = torch.empty((L, B, k), dtype=torch.int32, device=dev)
+    tsc = torch.empty((L, B, k), dtype=torch.float32, device=dev)
+    ws_topk = torch.empty(max(msa.msa_topk_docs_workspace_size(L, B, n_docs, k), 256), dtype=torch.uint8, device=dev)
+    ck = torch.empty((L, B, max_ctx, 8, 128), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    cl = torch.empty((L, B), dtype=torch.int32, device=dev)
+    out = torch.empty((L, B, Hq, 128), dtype=torch.float32, device=dev)
+    ws_dec = torch.empty(msa.msa_sparse_decode_workspace_size(L, B, Hq, max_ctx, cfg.L_loc), dtype=torch.uint8,
+                         device=dev)
+    scale = 1.0 / math.sqrt(128.0)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+    print("bench: %s memory ready in %.1f s (%d blocks x %d layers, %d docs, %.1f GB on device)"
+          % (cfg.name, t_setup, n_blk, L, n_docs, torch.cuda.memory_allocated() / 1e9), file=sys.stderr, flush=True)
+
+    n_ev = 6
+    def step(evs=None):
+        rec = (lambda i: evs[i].record()) if evs is not None else (lambda i: None)
+        rec(0)
+        if pool_args is not None:
+            msa.msa_pool_blocks(*pool_args)
+        rec(1)
+        msa.msa_route_scores(qr, krt, krn, n_blk, blk_doc, n_docs, dsc)
+        rec(2)
+        msa.msa_topk_docs(dsc, k, ids, tsc, ws_topk)
+        rec(3)
+        msa.msa_gather_ctx(ids, blk_d, max_db, kbar, vbar, ck, cv, cl)
+        rec(4)
+        msa.msa_sparse_decode(q, ck, cv, cl, lk, lv, ll, scale, out, ws_dec)
+        rec(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(n_ev - 1)]
+                    for i in range(args.steps)])            # ms
+    seg_mean = seg.mean(axis=0)
+    ms_step = wall * 1e3 / args.steps
+
+    # sanity of the result (cheap, outside the timed region): planted needles are the top-k
+    nd = S.needle_docs(cfg)
+    ids_h = ids.cpu().numpy()
+    needle_ok = all(set(ids_h[l, b].tolist()) == set(nd[b].tolist())
+                    for l in range(L) for b in range(nd.shape[0])) if cfg.needles == k else None
+
+    scan_bytes = L * n_blk * SCAN_BYTES_PER_BLOCK_LAYER
+    value = scan_bytes * args.steps / wall / 1e9                       # GB/s over whole steps
+    scan_ms = float(seg_mean[1])
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    ctx_rows = int(cl.sum().item())
+    dec_rows = ctx_rows + int(ll.sum().item())
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.description,
+            "layers": L, "blocks_per_layer": n_blk, "docs": n_docs, "queries": B, "query_tokens": T,
+            "top_k": k, "kv_heads": 8, "head_dim": 128, "q_heads": Hq, "local_rows": cfg.L_loc,
+            "route_key_bytes": L * tiles * 16 * 2048, "content_kv_bytes": 2 * L * n_blk * 2048,
+        },
+        "hbm_frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+        "ms_per_query_18_layers": round(ms_step / B, 4),
+        "ms_per_query_per_layer": round(ms_step / B / L, 5),
+        "scan_ms": round(scan_ms, 4),
+        "scan_ms_per_layer": round(scan_ms / L, 5),
+        "blocks_scanned_per_s": round(L * n_blk * B / (scan_ms * 1e-3), 1),
+        "breakdown_ms": {"pool": round(float(seg_mean[0]), 4), "route_scan": round(scan_ms, 4),
+                         "topk": round(float(seg_mean[2]), 4), "gather": round(float(seg_mean[3]), 4),
+                         "decode": round(float(seg_mean[4]), 4)},
+        "decode_us_per_token": round(float(seg_mean[4]) * 1e3, 2),
+        "decode_rows": dec_rows,
+        "needles_are_topk": needle_ok,
+        "roofline": {"bound": "hbm", "kernel": "route_mfma_kernel (msa_route_scores)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+    if cfg.per_token:
+        pool_ms = float(seg_mean[0])
+        result["pooled_tokens_per_s"] = round(L * n_tok / (pool_ms * 1e-3), 1)
+        result["pool_GBps"] = round(L * n_tok * POOL_BYTES_PER_TOKEN / (pool_ms * 1e-3) / 1e9, 2)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, n_blk, blk.numpy(), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, n_blk, blk_off, seconds):
+    """The fp64 oracle's routing scan on a bounded sample of the same memory (layer 0, the
+    first documents, the same query), one thread, scaled to GB/s of route keys scanned."""
+    import numpy as np
+
+    import oracle as O
+    from synth import synth as S
+
+    mem = S.memory_config(cfg)
+    q = S.qr_host(cfg, 0)[0, :cfg.T]
+    # calibrate on a few documents, then size the sample to ~`seconds`
+    def run(n_docs):
+        nb = int(blk_off[n_docs])
+        if cfg.per_token:
+            return None
+        rows = S.rows_host(mem.seed, S.S_KRBAR, 0, n_blk, 0, nb)
+        nrows, nq = S.needle_row_table(mem, blk_off)
+        sel = nrows < nb
+        if sel.any():
+            qmem = S.qr_host(mem, 0).reshape(-1, 8, 128)
+            rows[nrows[sel]] = S.needle_rows_host(mem.seed, 0, n_blk, nrows[sel], qmem[nq[sel]])
+        t = time.perf_counter()
+        O.doc_scores(q, rows, blk_off[: n_docs + 1])
+        return nb, time.perf_counter() - t
+
+    if cfg.per_token:
+        return None
+    nb, dt = run(20)
+    n_docs = int(min(len(blk_off) - 1, max(20, 20 * seconds / max(dt, 1e-6))))
+    nb, dt = run(n_docs)
+    gbps = nb * SCAN_BYTES_PER_BLOCK_LAYER / dt / 1e9
+    return {"value": round(gbps, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "fp64 oracle routing scan of layer 0, documents 0..%d (%d blocks) of the same memory, "
+                      "same %d-token query, single thread, %.1f s" % (n_docs - 1, nb, cfg.T, dt),
+            "blocks_per_s": round(nb / dt, 1)}
+
+
+if __name__ == "__main__":
+    main()

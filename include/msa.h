@@ -128,6 +128,15 @@ int msa_pool_blocks(int32_t n_layers, const uint16_t* k, const uint16_t* v, cons
 int msa_pack_route_keys(int32_t n_layers, const uint16_t* krbar_rows, int64_t n_blk,
                         uint16_t* krbar_route, float* krbar_norm, void* stream);
 
+/* Block -> document map of a memory: blk_doc[n] = the document whose block range
+ * [doc_blk_off[d], doc_blk_off[d+1]) holds block n, -1 for the padding blocks of
+ * the last route tile (or for blocks no document covers).  Built once per memory
+ * bank next to the route keys; it keys the per-document max of the routing scan.
+ *   doc_blk_off  [n_docs + 1] int64, device;  blk_doc [msa_route_tiles(n_blk) * 16] int32, output
+ * Errors: NULL pointers, n_docs < 1, n_blk < 0. */
+int msa_block_doc_map(const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk, int32_t* blk_doc,
+                      void* stream);
+
 /* --------------------------------------------------------------- A2: routing scan
  *
  * [P1 架构; P2 3.3.3, 5.2; P5 方法拆解] For each layer l, query b, query token t and
@@ -139,21 +148,18 @@ int msa_pack_route_keys(int32_t n_layers, const uint16_t* krbar_rows, int64_t n_
  *
  *   qr           [n_layers][B][T][8][128] bf16
  *   krbar_route, krbar_norm   route-key layout of n_blk blocks per layer
- *   doc_blk_off  [n_docs + 1] int64, device
+ *   blk_doc      block -> document map (msa_block_doc_map) of the same memory
  *   doc_scores   [n_layers][B][n_docs] fp32, output (accumulate = 0) or in/out
  *                (accumulate = 1: the result is max(previous value, new scores),
  *                i.e. the scores of the query rows seen so far plus these T rows;
  *                this is how a query grown by appended rows is re-routed exactly)
- *   workspace    >= msa_route_scores_workspace_size(n_blk) bytes
  *
  * Queries with T >= 16 use bf16 matrix cores (fp32 accumulate); shorter ones use
- * vector dot products.  Errors: NULL pointers, n_layers/B/T/n_docs < 1, n_blk < 0,
- * small workspace. */
-size_t msa_route_scores_workspace_size(int64_t n_blk);
+ * vector dot products.  Errors: NULL pointers, n_layers/B/T/n_docs < 1, n_blk < 0. */
 int msa_route_scores(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
                      const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
-                     const int64_t* doc_blk_off, int32_t n_docs, int32_t accumulate,
-                     float* doc_scores, void* workspace, size_t workspace_bytes, void* stream);
+                     const int32_t* blk_doc, int32_t n_docs, int32_t accumulate,
+                     float* doc_scores, void* stream);
 
 /* ---------------------------------------------------------------- A3: top-k docs
  *
@@ -173,11 +179,10 @@ int msa_topk_docs(int32_t n_layers, int32_t B, const float* doc_scores, int32_t 
 
 /* A2 then A3 with the document scores kept in the workspace (doc_scores may be
  * NULL; if given it receives a copy of them). */
-size_t msa_route_topk_workspace_size(int32_t n_layers, int32_t B, int32_t n_docs, int64_t n_blk,
-                                     int32_t k);
+size_t msa_route_topk_workspace_size(int32_t n_layers, int32_t B, int32_t n_docs, int32_t k);
 int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
                    const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
-                   const int64_t* doc_blk_off, int32_t n_docs, int32_t k,
+                   const int32_t* blk_doc, int32_t n_docs, int32_t k,
                    int32_t* topk_ids, float* topk_scores, float* doc_scores,
                    void* workspace, size_t workspace_bytes, void* stream);
 

@@ -140,37 +140,38 @@ MSA_API int msa_pack_route_keys(int32_t n_layers, const uint16_t* krbar_rows, in
 
 // ------------------------------------------------------------------------ A2
 
-MSA_API size_t msa_route_scores_workspace_size(int64_t n_blk) {
-  if (n_blk < 0) return 0;
-  return align256((size_t)msa::route_tiles(n_blk) * 16 * sizeof(int32_t)) + 256;
+MSA_API int msa_block_doc_map(const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk, int32_t* blk_doc,
+                              void* stream) {
+  if (!doc_blk_off || !blk_doc) return fail(MSA_ERR_NULL, "msa_block_doc_map: null pointer");
+  if (n_docs < 1 || n_blk < 0)
+    return fail(MSA_ERR_SHAPE, "msa_block_doc_map: n_docs=%d n_blk=%lld", n_docs, (long long)n_blk);
+  if (n_blk >= (int64_t)INT32_MAX - 32) return fail(MSA_ERR_UNSUPPORTED, "msa_block_doc_map: n_blk too large");
+  return hip_status(msa::launch_blk_doc(doc_blk_off, n_docs, n_blk, blk_doc, as_stream(stream)),
+                    "msa_block_doc_map");
 }
 
 static int check_route_args(const char* fn, int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
                             const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
-                            const int64_t* doc_blk_off, int32_t n_docs) {
-  if (!qr || !krbar_route || !krbar_norm || !doc_blk_off) return fail(MSA_ERR_NULL, "%s: null pointer", fn);
+                            const int32_t* blk_doc, int32_t n_docs) {
+  if (!qr || !krbar_route || !krbar_norm || !blk_doc) return fail(MSA_ERR_NULL, "%s: null pointer", fn);
   if (n_layers < 1 || B < 1 || T < 1 || n_docs < 1 || n_blk < 0)
     return fail(MSA_ERR_SHAPE, "%s: n_layers=%d B=%d T=%d n_docs=%d n_blk=%lld", fn, n_layers, B, T, n_docs,
                 (long long)n_blk);
   if (n_blk >= (int64_t)INT32_MAX - 32) return fail(MSA_ERR_UNSUPPORTED, "%s: n_blk too large", fn);
   if ((int64_t)B * ((T + 63) / 64) > INT32_MAX / 64) return fail(MSA_ERR_UNSUPPORTED, "%s: B*T too large", fn);
+  if (T < 16 && ((int64_t)n_layers > 65535 || B > 65535))
+    return fail(MSA_ERR_UNSUPPORTED, "%s: n_layers or B > 65535", fn);
   return MSA_OK;
 }
 
 MSA_API int msa_route_scores(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T, const uint16_t* krbar_route,
-                             const float* krbar_norm, int64_t n_blk, const int64_t* doc_blk_off, int32_t n_docs,
-                             int32_t accumulate, float* doc_scores, void* workspace, size_t workspace_bytes,
-                             void* stream) {
-  int st = check_route_args("msa_route_scores", n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, doc_blk_off,
-                            n_docs);
+                             const float* krbar_norm, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs,
+                             int32_t accumulate, float* doc_scores, void* stream) {
+  int st = check_route_args("msa_route_scores", n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs);
   if (st) return st;
-  if (!doc_scores || !workspace) return fail(MSA_ERR_NULL, "msa_route_scores: null pointer");
-  const size_t need = msa_route_scores_workspace_size(n_blk);
-  if (workspace_bytes < need)
-    return fail(MSA_ERR_WORKSPACE, "msa_route_scores: workspace %zu < %zu bytes", workspace_bytes, need);
-  return hip_status(msa::launch_route_scores(n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, doc_blk_off, n_docs,
-                                             accumulate ? 1 : 0, doc_scores, reinterpret_cast<int32_t*>(workspace),
-                                             as_stream(stream)),
+  if (!doc_scores) return fail(MSA_ERR_NULL, "msa_route_scores: null pointer");
+  return hip_status(msa::launch_route_scores(n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs,
+                                             accumulate ? 1 : 0, doc_scores, as_stream(stream)),
                     "msa_route_scores");
 }
 
@@ -199,41 +200,34 @@ MSA_API int msa_topk_docs(int32_t n_layers, int32_t B, const float* doc_scores, 
 
 // ------------------------------------------------------------------ A2 + A3
 
-MSA_API size_t msa_route_topk_workspace_size(int32_t n_layers, int32_t B, int32_t n_docs, int64_t n_blk, int32_t k) {
-  if (n_layers < 1 || B < 1 || n_docs < 1 || k < 1 || n_blk < 0) return 0;
+MSA_API size_t msa_route_topk_workspace_size(int32_t n_layers, int32_t B, int32_t n_docs, int32_t k) {
+  if (n_layers < 1 || B < 1 || n_docs < 1 || k < 1) return 0;
   const size_t scores = align256((size_t)n_layers * B * n_docs * sizeof(float));
-  const size_t a = msa_route_scores_workspace_size(n_blk);
-  const size_t b = msa_topk_docs_workspace_size(n_layers, B, n_docs, k);
-  return scores + (a > b ? a : b);
+  return scores + msa_topk_docs_workspace_size(n_layers, B, n_docs, k);
 }
 
 MSA_API int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T, const uint16_t* krbar_route,
-                           const float* krbar_norm, int64_t n_blk, const int64_t* doc_blk_off, int32_t n_docs,
+                           const float* krbar_norm, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs,
                            int32_t k, int32_t* topk_ids, float* topk_scores, float* doc_scores, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  int st = check_route_args("msa_route_topk", n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, doc_blk_off,
-                            n_docs);
+  int st = check_route_args("msa_route_topk", n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs);
   if (st) return st;
   if (!topk_ids || !workspace) return fail(MSA_ERR_NULL, "msa_route_topk: null pointer");
   if (k < 1 || k > n_docs) return fail(MSA_ERR_SHAPE, "msa_route_topk: k=%d n_docs=%d", k, n_docs);
   if (k > MSA_MAX_TOPK) return fail(MSA_ERR_UNSUPPORTED, "msa_route_topk: k=%d > %d", k, MSA_MAX_TOPK);
   if ((int64_t)n_layers * B > 65535) return fail(MSA_ERR_UNSUPPORTED, "msa_route_topk: n_layers*B > 65535");
-  const size_t need = msa_route_topk_workspace_size(n_layers, B, n_docs, n_blk, k);
+  const size_t need = msa_route_topk_workspace_size(n_layers, B, n_docs, k);
   if (workspace_bytes < need)
     return fail(MSA_ERR_WORKSPACE, "msa_route_topk: workspace %zu < %zu bytes", workspace_bytes, need);
   char* ws = reinterpret_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws);
+  float* scores = doc_scores ? doc_scores : reinterpret_cast<float*>(ws);
   char* rest = ws + align256((size_t)n_layers * B * n_docs * sizeof(float));
   hipStream_t s = as_stream(stream);
-  hipError_t e = msa::launch_route_scores(n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, doc_blk_off, n_docs, 0,
-                                          scores, reinterpret_cast<int32_t*>(rest), s);
+  hipError_t e = msa::launch_route_scores(n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs, 0,
+                                          scores, s);
   if (e != hipSuccess) return hip_status(e, "msa_route_topk (scores)");
   e = msa::launch_topk((int64_t)n_layers * B, scores, n_docs, k, topk_ids, topk_scores, rest, s);
   if (e != hipSuccess) return hip_status(e, "msa_route_topk (top-k)");
-  if (doc_scores) {
-    e = hipMemcpyAsync(doc_scores, scores, (size_t)n_layers * B * n_docs * sizeof(float), hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return hip_status(e, "msa_route_topk (copy scores)");
-  }
   return MSA_OK;
 }
 

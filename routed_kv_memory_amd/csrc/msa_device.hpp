@@ -87,9 +87,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 // (lanes >= n pass doc = -1).  Blocks of a document are contiguous, so a
 // segmented suffix max inside each run leaves the run's max in its first lane,
 // which folds it into the document score with one atomic max on its code.
-__device__ __forceinline__ void flush_doc_max(float v, int32_t doc, int n, uint32_t* __restrict__ codes) {
+__device__ __forceinline__ void flush_doc_max(float v, int32_t doc, int n, int32_t n_docs,
+                                              uint32_t* __restrict__ codes) {
   const int lane = __lane_id();
-  if (lane >= n) doc = -1;
+  if (lane >= n || doc >= n_docs) doc = -1;   // map entries are trusted only inside [0, n_docs)
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     float vo = __shfl_down(v, off, 64);

@@ -265,7 +265,7 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
           float v = __shfl(m[mt][q], src, 64);
           if ((lane >> 4) == mt && (lane & 3) == q) mine = v;
         }
-      flush_doc_max(mine, doc, 32, lcodes);
+      flush_doc_max(mine, doc, 32, n_docs, lcodes);
     }
     seg = seg_end;
   }
@@ -341,7 +341,7 @@ route_valu_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, const u
   m *= 0.125f;
   const int64_t blk = tile * kTile + lane;
   const int32_t doc = (lane < kTile) ? blk_doc[blk] : -1;
-  flush_doc_max(m, doc, kTile, codes + ((int64_t)layer * B + b) * n_docs);
+  flush_doc_max(m, doc, kTile, n_docs, codes + ((int64_t)layer * B + b) * n_docs);
 }
 
 int choose_ranges(int C, int cus) {
@@ -361,20 +361,26 @@ int choose_ranges(int C, int cus) {
 
 }  // namespace
 
+hipError_t launch_blk_doc(const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk, int32_t* blk_doc,
+                          hipStream_t s) {
+  const int64_t n_pad = route_tiles(n_blk) * kTile;
+  if (n_pad == 0) return hipSuccess;
+  const int grid = (int)((n_pad + 255) / 256 < 65536 ? (n_pad + 255) / 256 : 65536);
+  hipLaunchKernelGGL(blk_doc_kernel, dim3(grid), dim3(256), 0, s, doc_blk_off, n_docs, n_blk, n_pad, blk_doc);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_scores(int32_t L, const uint16_t* qr, int32_t B, int32_t T, const uint16_t* krt,
-                               const float* krn, int64_t n_blk, const int64_t* doc_blk_off, int32_t n_docs,
-                               int32_t accumulate, float* doc_scores, int32_t* blk_doc, hipStream_t s) {
+                               const float* krn, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs,
+                               int32_t accumulate, float* doc_scores, hipStream_t s) {
   const int64_t tiles = route_tiles(n_blk);
-  const int64_t n_pad = tiles * kTile;
   const int64_t n_codes = (int64_t)L * B * n_docs;
   uint32_t* codes = reinterpret_cast<uint32_t*>(doc_scores);
   const DeviceInfo di = device_info();
-  const int fill_grid = di.cus * 4;
+  const int fill_grid = (int)((n_codes + 255) / 256 < di.cus * 4 ? (n_codes + 255) / 256 : di.cus * 4);
 
   hipLaunchKernelGGL(codes_init_kernel, dim3(fill_grid), dim3(256), 0, s, codes, n_codes, accumulate);
-  if (n_pad > 0) {
-    hipLaunchKernelGGL(blk_doc_kernel, dim3(fill_grid), dim3(256), 0, s, doc_blk_off, n_docs, n_blk, n_pad,
-                       blk_doc);
+  if (tiles > 0) {
     if (T >= 16) {
       const int n_tc = (T + kTokChunk - 1) / kTokChunk;
       const int C = B * n_tc;

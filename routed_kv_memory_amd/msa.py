@@ -36,11 +36,11 @@ _SIGS = {
     "msa_route_tiles": ([_I64], _I64),
     "msa_pool_blocks": ([_I32, _P, _P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "msa_pack_route_keys": ([_I32, _P, _I64, _P, _P, _P], ctypes.c_int),
-    "msa_route_scores_workspace_size": ([_I64], _SZ),
-    "msa_route_scores": ([_I32, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+    "msa_block_doc_map": ([_P, _I32, _I64, _P, _P], ctypes.c_int),
+    "msa_route_scores": ([_I32, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I32, _P, _P], ctypes.c_int),
     "msa_topk_docs_workspace_size": ([_I32, _I32, _I32, _I32], _SZ),
     "msa_topk_docs": ([_I32, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
-    "msa_route_topk_workspace_size": ([_I32, _I32, _I32, _I64, _I32], _SZ),
+    "msa_route_topk_workspace_size": ([_I32, _I32, _I32, _I32], _SZ),
     "msa_route_topk": ([_I32, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
                        ctypes.c_int),
     "msa_gather_ctx": ([_I32, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _I64, _I32, _P, _P, _P, _P], ctypes.c_int),
@@ -159,19 +159,19 @@ def msa_pack_route_keys(krbar_rows, n_blk, krbar_route, krbar_norm, stream=None)
         _ptr(krbar_norm, _F32T, "krbar_norm"), _stream(stream)))
 
 
-def msa_route_scores_workspace_size(n_blk: int) -> int:
-    return int(lib().msa_route_scores_workspace_size(n_blk))
+def msa_block_doc_map(doc_blk_off, n_blk, blk_doc, stream=None):
+    n_docs = doc_blk_off.numel() - 1
+    _check("msa_block_doc_map", lib().msa_block_doc_map(
+        _ptr(doc_blk_off, _I64T, "doc_blk_off"), n_docs, n_blk, _ptr(blk_doc, _I32T, "blk_doc"), _stream(stream)))
 
 
-def msa_route_scores(qr, krbar_route, krbar_norm, n_blk, doc_blk_off, doc_scores, workspace, accumulate=False,
+def msa_route_scores(qr, krbar_route, krbar_norm, n_blk, blk_doc, n_docs, doc_scores, accumulate=False,
                      stream=None):
     L, B, T = qr.shape[0], qr.shape[1], qr.shape[2]
-    n_docs = doc_blk_off.numel() - 1
     _check("msa_route_scores", lib().msa_route_scores(
         L, _ptr(qr, _BF16, "qr"), B, T, _ptr(krbar_route, _BF16, "krbar_route"),
-        _ptr(krbar_norm, _F32T, "krbar_norm"), n_blk, _ptr(doc_blk_off, _I64T, "doc_blk_off"), n_docs,
-        1 if accumulate else 0, _ptr(doc_scores, _F32T, "doc_scores"), _ptr(workspace, _ANY, "workspace"),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(krbar_norm, _F32T, "krbar_norm"), n_blk, _ptr(blk_doc, _I32T, "blk_doc"), n_docs,
+        1 if accumulate else 0, _ptr(doc_scores, _F32T, "doc_scores"), _stream(stream)))
 
 
 def msa_topk_docs_workspace_size(n_layers, B, n_docs, k) -> int:
@@ -186,17 +186,16 @@ def msa_topk_docs(doc_scores, k, topk_ids, topk_scores, workspace, stream=None):
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def msa_route_topk_workspace_size(n_layers, B, n_docs, n_blk, k) -> int:
-    return int(lib().msa_route_topk_workspace_size(n_layers, B, n_docs, n_blk, k))
+def msa_route_topk_workspace_size(n_layers, B, n_docs, k) -> int:
+    return int(lib().msa_route_topk_workspace_size(n_layers, B, n_docs, k))
 
 
-def msa_route_topk(qr, krbar_route, krbar_norm, n_blk, doc_blk_off, k, topk_ids, topk_scores, workspace,
+def msa_route_topk(qr, krbar_route, krbar_norm, n_blk, blk_doc, n_docs, k, topk_ids, topk_scores, workspace,
                    doc_scores=None, stream=None):
     L, B, T = qr.shape[0], qr.shape[1], qr.shape[2]
-    n_docs = doc_blk_off.numel() - 1
     _check("msa_route_topk", lib().msa_route_topk(
         L, _ptr(qr, _BF16, "qr"), B, T, _ptr(krbar_route, _BF16, "krbar_route"),
-        _ptr(krbar_norm, _F32T, "krbar_norm"), n_blk, _ptr(doc_blk_off, _I64T, "doc_blk_off"), n_docs, k,
+        _ptr(krbar_norm, _F32T, "krbar_norm"), n_blk, _ptr(blk_doc, _I32T, "blk_doc"), n_docs, k,
         _ptr(topk_ids, _I32T, "topk_ids"), _ptr(topk_scores, _F32T, "topk_scores", allow_none=True),
         _ptr(doc_scores, _F32T, "doc_scores", allow_none=True), _ptr(workspace, _ANY, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -49,14 +49,23 @@ def pack_rows(rows: torch.Tensor, n_blk: int):
     return krt, krn
 
 
-def route(qr, krt, krn, n_blk, blk_off_d, k, dev="cuda"):
+def doc_map(blk_off_d: torch.Tensor, n_blk: int) -> torch.Tensor:
+    tiles = msa.msa_route_tiles(n_blk)
+    m = torch.empty(max(tiles, 1) * 16, dtype=torch.int32, device=blk_off_d.device)
+    msa.msa_block_doc_map(blk_off_d, n_blk, m)
+    return m
+
+
+def route(qr, krt, krn, n_blk, blk_off_d, k, dev="cuda", blk_doc=None):
     L, B = qr.shape[0], qr.shape[1]
     n_docs = blk_off_d.numel() - 1
-    ws = torch.empty(msa.msa_route_topk_workspace_size(L, B, n_docs, n_blk, k), dtype=torch.uint8, device=dev)
+    if blk_doc is None:
+        blk_doc = doc_map(blk_off_d, n_blk)
+    ws = torch.empty(msa.msa_route_topk_workspace_size(L, B, n_docs, k), dtype=torch.uint8, device=dev)
     ids = torch.empty((L, B, k), dtype=torch.int32, device=dev)
     sc = torch.empty((L, B, k), dtype=torch.float32, device=dev)
     dsc = torch.empty((L, B, n_docs), dtype=torch.float32, device=dev)
-    msa.msa_route_topk(qr, krt, krn, n_blk, blk_off_d, k, ids, sc, ws, doc_scores=dsc)
+    msa.msa_route_topk(qr, krt, krn, n_blk, blk_doc, n_docs, k, ids, sc, ws, doc_scores=dsc)
     return ids, sc, dsc
 
 

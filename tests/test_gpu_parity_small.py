@@ -25,7 +25,7 @@ def _gpu():
 
 
 from gpu_common import (SCORE_TOL, SCALE, alloc_route_keys, assert_decode, assert_topk, decode_all,  # noqa: E402
-                        gather_all, pack_rows, route, to_dev_bf16, u16, untile_keys, untile_norms)
+                        doc_map, gather_all, pack_rows, route, to_dev_bf16, u16, untile_keys, untile_norms)
 from routed_kv_memory_amd import msa  # noqa: E402
 
 
@@ -105,7 +105,7 @@ def test_route_scores_and_topk_shapes(T, B):
     qr = rand_bf16(rng, (L, B, T, 8, 128))
     # one block equal to a query token -> score 1 for that document (per layer)
     rows[0, off[5]] = qr[0, 0, T - 1]
-    rows[1, off[30] + 1] = qr[1, B - 1, 0]
+    rows[1, off[31] - 1] = qr[1, B - 1, 0]   # last block of doc 30
     krt, krn = pack_rows(to_dev_bf16(rows), n_blk)
     blk_d = torch.from_numpy(off).to(DEV)
     k = 7
@@ -135,13 +135,13 @@ def test_route_accumulate_equals_full_query():
     blk_d = torch.from_numpy(off).to(DEV)
     qr = rand_bf16(rng, (L, B, 64 + 128, 8, 128))
     n_docs = len(off) - 1
-    ws = torch.empty(msa.msa_route_scores_workspace_size(n_blk), dtype=torch.uint8, device=DEV)
+    m = doc_map(blk_d, n_blk)
     full = torch.empty((L, B, n_docs), dtype=torch.float32, device=DEV)
-    msa.msa_route_scores(to_dev_bf16(qr), krt, krn, n_blk, blk_d, full, ws)
+    msa.msa_route_scores(to_dev_bf16(qr), krt, krn, n_blk, m, n_docs, full)
     inc = torch.empty_like(full)
-    msa.msa_route_scores(to_dev_bf16(qr[:, :, :64]), krt, krn, n_blk, blk_d, inc, ws)
+    msa.msa_route_scores(to_dev_bf16(qr[:, :, :64]), krt, krn, n_blk, m, n_docs, inc)
     first = inc.clone()
-    msa.msa_route_scores(to_dev_bf16(qr[:, :, 64:]), krt, krn, n_blk, blk_d, inc, ws, accumulate=True)
+    msa.msa_route_scores(to_dev_bf16(qr[:, :, 64:]), krt, krn, n_blk, m, n_docs, inc, accumulate=True)
     torch.cuda.synchronize()
     assert torch.equal(inc, full)
     assert bool((inc >= first).all())
