@@ -28,8 +28,6 @@
 namespace msa {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kWG = kWaves * 64;
 constexpr int kTokChunk = 64;
 constexpr int kTileU4 = kTileElems / 8;   // 2048 uint4 per tile
 constexpr int kHeadU4 = kTileU4 / kHeads; // 256 uint4 per (tile, head)
@@ -80,17 +78,37 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 
 // ---------------------------------------------------------------- MFMA scan
 //
-// Work item = one 32-block wave tile (route tiles 2w, 2w+1) of one layer.
-// Accumulator layout of v_mfma_f32_16x16x32_bf16 (A = 16 blocks x 32 dims,
-// B = 32 dims x 16 tokens): lane l holds token (l & 15) and blocks 4*(l >> 4) + r.
+// One workgroup per CU, 8 waves: wave h owns KV head h.  It keeps the query
+// chunk's head-h fragments (64 tokens x 128 dims, the B operand of
+// v_mfma_f32_16x16x32_bf16) and their inverse norms in registers for the whole
+// layer, and streams only its own head's 4 KiB of each 16-block route tile (four
+// contiguous 1 KiB A-operand fragments), prefetched three tiles ahead in
+// registers.  Per tile it scales its 16 blocks x 64 tokens of dot products by
+// 1/(|q| |k|) and writes them to LDS; after a barrier, wave n sums the 8 heads for
+// token group n, takes the max over its 16 tokens with a DPP row reduction, and
+// wave 0 folds the four token groups into per-document maxima.
+//
+// Accumulator layout (A = 16 blocks x 32 dims, B = 32 dims x 16 tokens): lane l
+// holds token (l & 15) and blocks 4*(l >> 4) + r, r = 0..3.
+constexpr int kScanWaves = kHeads;              // one wave per KV head
+constexpr int kScanWG = kScanWaves * 64;
+constexpr int kPrefetch = 3;                     // tiles in flight per wave beyond the current one
+
+__device__ __forceinline__ void lds_barrier() {
+  // orders LDS only: in-flight global prefetches stay in flight across the barrier
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int NT>
-__global__ void __launch_bounds__(kWG)
+__global__ void __launch_bounds__(kScanWG)
 route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t n_tc,
-                  const uint4* __restrict__ krt, const float4* __restrict__ krn, int64_t n_blk, int64_t tiles,
+                  const uint4* __restrict__ krt, const float4* __restrict__ krn, int64_t tiles,
                   const int32_t* __restrict__ blk_doc, int32_t n_docs, int32_t L, int32_t R,
                   uint32_t* __restrict__ codes) {
-  __shared__ uint4 q_lds[kHeads * 4 * 4 * 64];   // [h][s][nt][lane] fragments, 128 KiB
-  __shared__ float rq_lds[kHeads * kTokChunk];   // [h][token] 1/max(|q|, eps)
+  __shared__ float4 P[2][kScanWaves][NT][64];   // per-head scaled partial scores of one tile
+  __shared__ float M[2][4][kTile];               // per token-group block maxima
 
   // XCD-aware placement: workgroups are dispatched round-robin over 8 XCDs; when the
   // ranges divide evenly, keep the chunks that share a range on one XCD (shared L2).
@@ -108,166 +126,138 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
     }
   }
   const int b = cidx / n_tc;
-  const int tc = cidx % n_tc;
-  const int t_base = tc * kTokChunk;
+  const int t_base = (cidx % n_tc) * kTokChunk;
 
-  const int64_t n_wt = (tiles + 1) >> 1;
-  const int64_t W = (int64_t)L * n_wt;
+  const int64_t W = (int64_t)L * tiles;          // items = (layer, tile)
   const int64_t it_begin = W * r / R;
   const int64_t it_end = W * (r + 1) / R;
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+  const int wave = threadIdx.x >> 6;             // = head
+  const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int j = lane & 15;
 
-  for (int64_t seg = it_begin; seg < it_end;) {
-    const int layer = (int)(seg / n_wt);
-    const int64_t lay_end = (int64_t)(layer + 1) * n_wt;
-    const int64_t seg_end = it_end < lay_end ? it_end : lay_end;
+  bf16x8 q[4][NT];       // [s][nt]
+  float rq[NT];
+  int cur_layer = -1;
 
-    // ---- stage this layer's query chunk in fragment order, then its inverse norms
-    __syncthreads();
-    const uint16_t* qbase = qr + (((int64_t)layer * B + b) * T) * kRow;
-    for (int f = tid; f < kHeads * 4 * 4 * 64; f += kWG) {
-      const int fl = f & 63, nt = (f >> 6) & 3, s = (f >> 8) & 3, h = f >> 10;
-      const int tok = t_base + nt * 16 + (fl & 15);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (nt < NT && tok < T)
-        v = *reinterpret_cast<const uint4*>(qbase + (int64_t)tok * kRow + h * kDim + s * 32 + (fl >> 4) * 8);
-      q_lds[f] = v;
+  if (it_begin >= it_end) return;   // uniform across the workgroup
+
+  // Prefetch cursor.  Items are consecutive, so the head's fragments and norms of
+  // item i sit at a linear offset; loads are unconditional (past the range end the
+  // last item is simply fetched again) so that every wait is an exact count.
+  const uint4* isrc = krt + it_begin * kTileU4 + wave * kHeadU4 + lane;
+  const float4* insrc = krn + (it_begin * kHeads + wave) * 4 + g;
+  int64_t itau = it_begin % tiles;
+  int64_t inext = it_begin;
+
+  uint4 kb[kPrefetch + 1][4];
+  float4 nb[kPrefetch + 1];
+  int32_t db[kPrefetch + 1];
+
+  auto issue = [&](uint4 (&kbuf)[4], float4& nbuf, int32_t& dbuf) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kbuf[s] = isrc[s * 64];
+    nbuf = *insrc;
+    dbuf = blk_doc[itau * kTile + j];
+    if (inext + 1 < it_end) {
+      ++inext;
+      isrc += kTileU4;
+      insrc += kHeads * 4;
+      itau = (itau + 1 == tiles) ? 0 : itau + 1;
     }
-    __syncthreads();
-    {
-      const int h = tid >> 6, tt = tid & 63;   // 512 threads = 8 heads x 64 tokens
-      const int nt = tt >> 4;
-      float ss = 0.f;
+  };
+
+#pragma unroll
+  for (int x = 0; x < kPrefetch; ++x) issue(kb[x], nb[x], db[x]);
+
+  // compute cursor
+  int layer = (int)(it_begin / tiles);
+  int64_t ctau = it_begin - (int64_t)layer * tiles;
+
+  for (int64_t base = it_begin; base < it_end; base += kPrefetch + 1) {
+#pragma unroll
+    for (int x = 0; x <= kPrefetch; ++x) {
+      const int64_t it = base + x;
+      constexpr int kNB = kPrefetch + 1;
+      issue(kb[(x + kPrefetch) % kNB], nb[(x + kPrefetch) % kNB], db[(x + kPrefetch) % kNB]);
+      if (it >= it_end) break;   // uniform across the workgroup
+
+      if (layer != cur_layer) {
+        // this layer's query chunk, head `wave`, as B fragments; inverse norms per token
+        const uint16_t* qb = qr + (((int64_t)layer * B + b) * T) * kRow + wave * kDim + g * 8;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int tok = t_base + nt * 16 + j;
+          float ss = 0.f;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (tok < T) v = *reinterpret_cast<const uint4*>(qb + (int64_t)tok * kRow + s * 32);
+            q[s][nt] = as_bf16x8(v);
+            const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float a = bf16_lo(p[e]), c = bf16_hi(p[e]);
+              ss += a * a + c * c;
+            }
+          }
+          ss += __shfl_xor(ss, 16, 64);
+          ss += __shfl_xor(ss, 32, 64);
+          rq[nt] = 1.0f / fmaxf(sqrtf(ss), kNormEps);
+        }
+        cur_layer = layer;
+      }
+
+      f32x4 acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          uint4 w = q_lds[((h * 4 + s) * 4 + nt) * 64 + gg * 16 + (tt & 15)];
-          const uint32_t p[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float a = bf16_lo(p[e]), c = bf16_hi(p[e]);
-            ss += a * a + c * c;
-          }
-        }
-      rq_lds[h * kTokChunk + tt] = 1.0f / fmaxf(sqrtf(ss), kNormEps);
-    }
-    __syncthreads();
+        for (int nt = 0; nt < NT; ++nt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[x][s]), q[s][nt], acc[nt], 0, 0, 0);
 
-    const uint4* kt = krt + (int64_t)layer * tiles * kTileU4;
-    const float4* kn = krn + (int64_t)layer * tiles * (kHeads * 4);
-    uint32_t* lcodes = codes + ((int64_t)layer * B + b) * n_docs;
-
-    for (int64_t it = seg + wave; it < seg_end; it += kWaves) {
-      const int64_t wt = it - (int64_t)layer * n_wt;
-      const int64_t tau0 = 2 * wt;
-      const bool has1 = (tau0 + 1) < tiles;
-      const int64_t blk_lane = tau0 * kTile + lane;
-      const int32_t doc = (lane < 32 && blk_lane < tiles * kTile) ? blk_doc[blk_lane] : -1;
-
-      f32x4 tot[2][NT];
+      const float4 kn4 = nb[x];
+      const float rk[4] = {__builtin_amdgcn_rcpf(fmaxf(kn4.x, kNormEps)), __builtin_amdgcn_rcpf(fmaxf(kn4.y, kNormEps)),
+                           __builtin_amdgcn_rcpf(fmaxf(kn4.z, kNormEps)), __builtin_amdgcn_rcpf(fmaxf(kn4.w, kNormEps))};
+      const int pb = x & 1;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) tot[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-      uint4 a_cur[2][4];
-      float4 n_cur[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bool ok = mt == 0 || has1;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          a_cur[mt][s] = ok ? kt[(tau0 + mt) * kTileU4 + 0 * kHeadU4 + s * 64 + lane] : make_uint4(0, 0, 0, 0);
-        n_cur[mt] = ok ? kn[((tau0 + mt) * kHeads + 0) * 4 + g] : make_float4(1.f, 1.f, 1.f, 1.f);
+      for (int nt = 0; nt < NT; ++nt) {
+        const float w = rq[nt];
+        P[pb][wave][nt][lane] = make_float4(acc[nt][0] * (w * rk[0]), acc[nt][1] * (w * rk[1]),
+                                            acc[nt][2] * (w * rk[2]), acc[nt][3] * (w * rk[3]));
       }
-
-#pragma unroll 1
-      for (int h = 0; h < kHeads; ++h) {
-        uint4 a_nxt[2][4];
-        float4 n_nxt[2];
-        if (h + 1 < kHeads) {
+      lds_barrier();
+      if (wave < NT) {
+        float4 tot = P[pb][0][wave][lane];
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const bool ok = mt == 0 || has1;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              a_nxt[mt][s] = ok ? kt[(tau0 + mt) * kTileU4 + (h + 1) * kHeadU4 + s * 64 + lane]
-                                : make_uint4(0, 0, 0, 0);
-            n_nxt[mt] = ok ? kn[((tau0 + mt) * kHeads + h + 1) * 4 + g] : make_float4(1.f, 1.f, 1.f, 1.f);
-          }
+        for (int h = 1; h < kHeads; ++h) {
+          const float4 v = P[pb][h][wave][lane];
+          tot.x += v.x; tot.y += v.y; tot.z += v.z; tot.w += v.w;
         }
-
-        f32x4 acc[2][NT];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const bf16x8 bq = as_bf16x8(q_lds[((h * 4 + s) * 4 + nt) * 64 + lane]);
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-              acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_cur[mt][s]), bq, acc[mt][nt],
-                                                                     0, 0, 0);
-          }
-        }
-        float rq[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) rq[nt] = rq_lds[h * kTokChunk + nt * 16 + j];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const float rk[4] = {__builtin_amdgcn_rcpf(fmaxf(n_cur[mt].x, kNormEps)),
-                               __builtin_amdgcn_rcpf(fmaxf(n_cur[mt].y, kNormEps)),
-                               __builtin_amdgcn_rcpf(fmaxf(n_cur[mt].z, kNormEps)),
-                               __builtin_amdgcn_rcpf(fmaxf(n_cur[mt].w, kNormEps))};
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) tot[mt][nt][q] += acc[mt][nt][q] * (rq[nt] * rk[q]);
-        }
-        if (h + 1 < kHeads) {
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) a_cur[mt][s] = a_nxt[mt][s];
-            n_cur[mt] = n_nxt[mt];
-          }
+        const bool valid = t_base + wave * 16 + j < T;
+        const float ninf = -__builtin_huge_valf();
+        const float m0 = row16_max(valid ? tot.x : ninf), m1 = row16_max(valid ? tot.y : ninf);
+        const float m2 = row16_max(valid ? tot.z : ninf), m3 = row16_max(valid ? tot.w : ninf);
+        if (j == 0) {
+          M[pb][wave][4 * g + 0] = m0 * 0.125f;   // head mean
+          M[pb][wave][4 * g + 1] = m1 * 0.125f;
+          M[pb][wave][4 * g + 2] = m2 * 0.125f;
+          M[pb][wave][4 * g + 3] = m3 * 0.125f;
         }
       }
-
-      // max over this chunk's valid tokens, then over the 16 token lanes of each row
-      float m[2][4];
+      lds_barrier();
+      if (wave == 0) {
+        float v = -__builtin_huge_valf();
+        if (lane < kTile) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float v = -__builtin_huge_valf();
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            if (t_base + nt * 16 + j < T) v = fmaxf(v, tot[mt][nt][q]);
-          m[mt][q] = row16_max(v) * 0.125f;   // head mean
+          for (int n = 0; n < NT; ++n) v = fmaxf(v, M[pb][n][lane]);
         }
-      // lane i < 32 takes block i of the wave tile: rows mt*16 + 4*g' + q live in lane 16*g'
-      float mine = -__builtin_huge_valf();
-      const int src = 16 * ((lane >> 2) & 3);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float v = __shfl(m[mt][q], src, 64);
-          if ((lane >> 4) == mt && (lane & 3) == q) mine = v;
-        }
-      flush_doc_max(mine, doc, 32, n_docs, lcodes);
+        flush_doc_max(v, db[x], kTile, n_docs, codes + ((int64_t)layer * B + b) * n_docs);
+      }
+      if (++ctau == tiles) { ctau = 0; ++layer; }
     }
-    seg = seg_end;
   }
 }
 
@@ -345,16 +335,18 @@ route_valu_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, const u
 }
 
 int choose_ranges(int C, int cus) {
-  // R ranges per chunk so that R*C workgroups fill whole waves of one workgroup per CU
+  // R ranges per query chunk; the persistent grid of R*C workgroups (one per CU at a
+  // time) should fill whole waves of the device: pick R in [ceil(cus/C), 4*ceil(cus/C)]
+  // with the best filled fraction, the smallest R on ties.
   if (C >= cus) return 1;
-  int best = 1;
+  const int r0 = (cus + C - 1) / C;
+  int best = r0;
   double best_eff = 0.0;
-  for (int R = 1; R <= 64; ++R) {
+  for (int R = r0; R <= 4 * r0; ++R) {
     const long total = (long)R * C;
     const long waves = (total + cus - 1) / cus;
     const double eff = (double)total / (double)(waves * cus);
     if (eff > best_eff + 1e-9) { best_eff = eff; best = R; }
-    if (eff >= 0.999) break;
   }
   return best;
 }
@@ -390,14 +382,14 @@ hipError_t launch_route_scores(int32_t L, const uint16_t* qr, int32_t B, int32_t
       const uint4* kt = reinterpret_cast<const uint4*>(krt);
       const float4* kn = reinterpret_cast<const float4*>(krn);
       switch (NT) {
-        case 1: hipLaunchKernelGGL(route_mfma_kernel<1>, grid, dim3(kWG), 0, s, qr, B, T, n_tc, kt, kn, n_blk,
-                                   tiles, blk_doc, n_docs, L, R, codes); break;
-        case 2: hipLaunchKernelGGL(route_mfma_kernel<2>, grid, dim3(kWG), 0, s, qr, B, T, n_tc, kt, kn, n_blk,
-                                   tiles, blk_doc, n_docs, L, R, codes); break;
-        case 3: hipLaunchKernelGGL(route_mfma_kernel<3>, grid, dim3(kWG), 0, s, qr, B, T, n_tc, kt, kn, n_blk,
-                                   tiles, blk_doc, n_docs, L, R, codes); break;
-        default: hipLaunchKernelGGL(route_mfma_kernel<4>, grid, dim3(kWG), 0, s, qr, B, T, n_tc, kt, kn, n_blk,
-                                    tiles, blk_doc, n_docs, L, R, codes); break;
+        case 1: hipLaunchKernelGGL(route_mfma_kernel<1>, grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, kn, tiles,
+                                   blk_doc, n_docs, L, R, codes); break;
+        case 2: hipLaunchKernelGGL(route_mfma_kernel<2>, grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, kn, tiles,
+                                   blk_doc, n_docs, L, R, codes); break;
+        case 3: hipLaunchKernelGGL(route_mfma_kernel<3>, grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, kn, tiles,
+                                   blk_doc, n_docs, L, R, codes); break;
+        default: hipLaunchKernelGGL(route_mfma_kernel<4>, grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, kn, tiles,
+                                    blk_doc, n_docs, L, R, codes); break;
       }
     } else {
       const dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)B, (unsigned)L);
