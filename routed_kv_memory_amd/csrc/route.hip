@@ -151,14 +151,16 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
   int64_t itau = it_begin % tiles;
   int64_t inext = it_begin;
 
-  uint4 kb[kPrefetch + 1][4];
-  float4 nb[kPrefetch + 1];
+  u32x4 kb[kPrefetch + 1][4];
+  f32x4 nb[kPrefetch + 1];
   int32_t db[kPrefetch + 1];
 
-  auto issue = [&](uint4 (&kbuf)[4], float4& nbuf, int32_t& dbuf) {
+  // The route keys and norms are read exactly once: non-temporal loads keep them
+  // from displacing useful lines in the caches.
+  auto issue = [&](u32x4 (&kbuf)[4], f32x4& nbuf, int32_t& dbuf) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kbuf[s] = isrc[s * 64];
-    nbuf = *insrc;
+    for (int s = 0; s < 4; ++s) kbuf[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(isrc + s * 64));
+    nbuf = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(insrc));
     dbuf = blk_doc[itau * kTile + j];
     if (inext + 1 < it_end) {
       ++inext;
@@ -216,11 +218,12 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[x][s]), q[s][nt], acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[x][s]), q[s][nt], acc[nt],
+                                                                  0, 0, 0);
 
-      const float4 kn4 = nb[x];
-      const float rk[4] = {__builtin_amdgcn_rcpf(fmaxf(kn4.x, kNormEps)), __builtin_amdgcn_rcpf(fmaxf(kn4.y, kNormEps)),
-                           __builtin_amdgcn_rcpf(fmaxf(kn4.z, kNormEps)), __builtin_amdgcn_rcpf(fmaxf(kn4.w, kNormEps))};
+      const f32x4 kn4 = nb[x];
+      const float rk[4] = {__builtin_amdgcn_rcpf(fmaxf(kn4[0], kNormEps)), __builtin_amdgcn_rcpf(fmaxf(kn4[1], kNormEps)),
+                           __builtin_amdgcn_rcpf(fmaxf(kn4[2], kNormEps)), __builtin_amdgcn_rcpf(fmaxf(kn4[3], kNormEps))};
       const int pb = x & 1;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {

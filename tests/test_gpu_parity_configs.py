@@ -1,0 +1,301 @@
+"""GPU parity at the full workload sizes (1M-, 10M-, 100M-token memories and the
+interleaved re-routing batch), in the launch configuration bench.py times.
+
+The oracle cannot redo these whole, so each step is checked on sampled outputs
+it computes one by one (pooled blocks, document scores, gathered contexts,
+decode rows), step-isolated on the GPU's previous output, plus properties that
+hold at any size: the planted needle documents are exactly the Top-16 where a
+query carries 16 needles, the selection is exact on the GPU's own scores, and
+re-routing a grown query only raises scores and equals the full recompute."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import synth as S
+from synth.device import DeviceInputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from routed_kv_memory_amd import msa
+    msa.lib()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+from gpu_common import (SCALE, SCORE_TOL, alloc_route_keys, assert_decode, assert_topk, decode_all,  # noqa: E402
+                        exact_topk_of, u16, untile_keys, untile_norms)
+from routed_kv_memory_amd import msa  # noqa: E402
+
+
+_NEEDLE_CACHE = {}
+
+
+def _needle_table(mem):
+    if mem.name not in _NEEDLE_CACHE:
+        off = S.prepooled_doc_blk_offsets(mem)
+        _NEEDLE_CACHE[mem.name] = S.needle_row_table(mem, off)
+    return _NEEDLE_CACHE[mem.name]
+
+
+def route_rows_host(mem, layer, b0, b1):
+    """Host copy of pre-pooled routing-key rows [b0, b1) of one layer, needles planted."""
+    rows = S.rows_host(mem.seed, S.S_KRBAR, layer, mem.n_blk, b0, b1)
+    nrows, nq = _needle_table(mem)
+    sel = (nrows >= b0) & (nrows < b1)
+    if sel.any():
+        q = S.qr_host(mem, layer).reshape(-1, 8, 128)
+        rows[nrows[sel] - b0] = S.needle_rows_host(mem.seed, layer, mem.n_blk, nrows[sel], q[nq[sel]])
+    return rows
+
+
+class Memory:
+    """Device memory of one workload, built the way bench.py builds it."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
+        self.di = DeviceInputs(cfg, DEV)
+        mem = self.di.mem
+        L = mem.n_layers
+        if mem.per_token:
+            self.tok, self.k, self.v, self.kr = self.di.per_token()
+            self.blk, self.n_blk, self.max_db = msa.msa_block_offsets_host(self.tok)
+        else:
+            self.blk = self.di.prepooled_offsets()
+            self.n_blk = int(self.blk[-1])
+            self.max_db = int((self.blk[1:] - self.blk[:-1]).max())
+        self.n_docs = self.blk.numel() - 1
+        self.blk_d = self.blk.to(DEV)
+        self.krt, self.krn = alloc_route_keys(L, self.n_blk)
+        if mem.per_token:
+            self.kbar = torch.empty((L, self.n_blk, 8, 128), dtype=torch.bfloat16, device=DEV)
+            self.vbar = torch.empty_like(self.kbar)
+            msa.msa_pool_blocks(self.k, self.v, self.kr, self.tok.to(DEV), self.blk_d, self.n_blk, self.kbar,
+                                self.vbar, self.krt, self.krn)
+        else:
+            self.kbar, self.vbar = self.di.prepooled_content()
+            for l, rows in self.di.prepooled_route_rows():
+                msa.msa_pack_route_keys(rows.view(1, self.n_blk, 8, 128), self.n_blk, self.krt[l:l + 1],
+                                        self.krn[l:l + 1])
+        tiles = msa.msa_route_tiles(self.n_blk)
+        self.blk_doc = torch.empty(tiles * 16, dtype=torch.int32, device=DEV)
+        msa.msa_block_doc_map(self.blk_d, self.n_blk, self.blk_doc)
+        torch.cuda.synchronize()
+
+    def route(self, qr, k, doc_scores=None, accumulate=False):
+        L, B = qr.shape[0], qr.shape[1]
+        if doc_scores is None:
+            doc_scores = torch.empty((L, B, self.n_docs), dtype=torch.float32, device=DEV)
+        msa.msa_route_scores(qr, self.krt, self.krn, self.n_blk, self.blk_doc, self.n_docs, doc_scores,
+                             accumulate=accumulate)
+        ids = torch.empty((L, B, k), dtype=torch.int32, device=DEV)
+        sc = torch.empty((L, B, k), dtype=torch.float32, device=DEV)
+        ws = torch.empty(max(msa.msa_topk_docs_workspace_size(L, B, self.n_docs, k), 256), dtype=torch.uint8,
+                         device=DEV)
+        msa.msa_topk_docs(doc_scores, k, ids, sc, ws)
+        return ids, sc, doc_scores
+
+    def gather(self, ids):
+        L, B, k = ids.shape
+        max_ctx = k * self.max_db
+        ck = torch.empty((L, B, max_ctx, 8, 128), dtype=torch.bfloat16, device=DEV)
+        cv = torch.empty_like(ck)
+        cl = torch.empty((L, B), dtype=torch.int32, device=DEV)
+        msa.msa_gather_ctx(ids, self.blk_d, self.max_db, self.kbar, self.vbar, ck, cv, cl)
+        return ck, cv, cl
+
+    def free(self):
+        for name in ("k", "v", "kr", "kbar", "vbar", "krt", "krn"):
+            if hasattr(self, name):
+                delattr(self, name)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def check_needles(cfg, ids_h):
+    nd = S.needle_docs(cfg)
+    if cfg.needles != cfg.k:
+        return
+    for l in range(ids_h.shape[0]):
+        for b in range(nd.shape[0]):
+            assert set(ids_h[l, b].tolist()) == set(nd[b].tolist()), (l, b)
+
+
+def check_gather_decode(m, ids, ck, cv, cl, q, lk, lv, ll, pairs):
+    ck_h_len = cl.cpu().numpy()
+    ids_h = ids.cpu().numpy()
+    out = decode_all(q, ck, cv, cl, lk, lv, ll)
+    torch.cuda.synchronize()
+    out_h = out.cpu().numpy()
+    off = m.blk.numpy()
+    for l, b in pairs:
+        sel = ids_h[l, b]
+        blocks = np.concatenate([np.arange(off[d], off[d + 1]) for d in sel])
+        n = int(ck_h_len[l, b])
+        assert n == blocks.size
+        kb = u16(m.kbar[l, torch.from_numpy(blocks).to(DEV)])
+        vb = u16(m.vbar[l, torch.from_numpy(blocks).to(DEV)])
+        got_k, got_v = u16(ck[l, b, :n]), u16(cv[l, b, :n])
+        assert np.array_equal(got_k, kb) and np.array_equal(got_v, vb)        # bit-exact gather
+        nl = int(ll[l, b].item())
+        ref = O.decode(u16(q[l, b]), got_k, got_v, u16(lk[l, b, :nl]), u16(lv[l, b, :nl]), SCALE)
+        assert_decode(out_h[l, b], ref)
+
+
+# ---------------------------------------------------------------------- 1M tokens, full path
+
+def test_1m_tokens_full_path():
+    cfg = S.CONFIGS["1m"]
+    print("case: 1M-token memory, full path (pool -> route -> gather -> decode)", flush=True)
+    m = Memory(cfg)
+    rng = np.random.default_rng(101)
+    tok = m.tok.numpy()
+    off = m.blk.numpy()
+    n_tok = int(tok[-1])
+    # A1 on sampled blocks (partial tails and needle documents included)
+    nd = S.needle_docs(cfg)[0]
+    docs = np.concatenate([rng.integers(0, m.n_docs, 24), nd[:4]])
+    krbar_cache = {}
+    for i, d in enumerate(docs):
+        l = int(rng.integers(0, cfg.n_layers))
+        for jb in {0, int(off[d + 1] - off[d] - 1)}:
+            blk = int(off[d] + jb)
+            t0, t1 = int(tok[d] + 64 * jb), int(min(tok[d] + 64 * jb + 64, tok[d + 1]))
+            for name, stream, got_t in (("K", S.S_K, m.kbar), ("V", S.S_V, m.vbar)):
+                x = S.rows_host(cfg.seed, stream, l, n_tok, t0, t1)
+                ref = O.pool(x[None], np.array([0, t1 - t0]), np.array([0, 1]))[0, 0]
+                got = u16(got_t[l, blk])
+                assert np.abs(ref.astype(np.int32) - got.astype(np.int32)).max() <= 1, (name, l, blk)
+            x = u16(m.kr[l, t0:t1])
+            assert np.array_equal(x[:1], S.rows_host(cfg.seed, S.S_KR, l, n_tok, t0, t0 + 1)) or d in nd
+            ref = O.pool(x[None], np.array([0, t1 - t0]), np.array([0, 1]))[0, 0]
+            tile = blk // 16
+            if (l, tile) not in krbar_cache:
+                krbar_cache[(l, tile)] = (untile_keys(m.krt[l:l + 1, tile * 16:(tile + 1) * 16], 16)[0],
+                                          untile_norms(m.krn[l:l + 1, tile * 16:(tile + 1) * 16], 16)[0])
+            kr_rows, kr_norms = krbar_cache[(l, tile)]
+            got = kr_rows[blk % 16]
+            assert np.abs(ref.astype(np.int32) - got.astype(np.int32)).max() <= 1, ("Kr", l, blk)
+            assert np.allclose(kr_norms[blk % 16], O.head_norms(got[None])[0], rtol=1e-6, atol=0)
+    # needle documents' Kr tokens are Qr + 0.3 z exactly as the generator defines
+    qr = m.di.qr()
+    d0 = int(nd[0])
+    got = u16(m.kr[3, int(tok[d0]):int(tok[d0]) + 3])
+    ref = S.needle_rows_host(cfg.seed, 3, n_tok, np.arange(tok[d0], tok[d0] + 3),
+                             np.repeat(u16(qr[3, 0, S.needle_token(0, cfg.T)])[None], 3, 0))
+    assert np.array_equal(got, ref)
+    # A2 + A3 (all layers: needles; two layers: every document against the oracle)
+    ids, sc, dsc = m.route(qr, cfg.k)
+    torch.cuda.synchronize()
+    ids_h, sc_h, dsc_h = ids.cpu().numpy(), sc.cpu().numpy(), dsc.cpu().numpy()
+    check_needles(cfg, ids_h)
+    for l in (0, cfg.n_layers - 1):
+        krbar = untile_keys(m.krt[l:l + 1], m.n_blk)[0]
+        S_o = O.doc_scores(u16(qr[l, 0]), krbar, off)
+        assert np.max(np.abs(S_o - dsc_h[l, 0])) < SCORE_TOL
+        assert_topk(ids_h[l, 0], sc_h[l, 0], dsc_h[l, 0], S_o, cfg.k)
+    # A4 + A5
+    ck, cv, cl = m.gather(ids)
+    q, lk, lv, ll = m.di.decode_inputs()
+    check_gather_decode(m, ids, ck, cv, cl, q, lk, lv, ll, [(0, 0), (7, 0), (17, 0)])
+    m.free()
+
+
+# ------------------------------------------------------------------ pre-pooled memories
+
+def prepooled_case(cfg_name, route_pairs, decode_pairs, n_random_docs):
+    cfg = S.CONFIGS[cfg_name]
+    print("case: %s memory, routing + decode on pre-pooled keys" % cfg_name, flush=True)
+    m = Memory(cfg)
+    off = m.blk.numpy()
+    rng = np.random.default_rng(202 + cfg.index)
+    # packed route keys: sampled tiles untile to the generated rows bit-exactly; norms match
+    for _ in range(6):
+        l = int(rng.integers(0, cfg.n_layers))
+        tile = int(rng.integers(0, msa.msa_route_tiles(m.n_blk)))
+        b1 = min((tile + 1) * 16, m.n_blk)
+        rows = route_rows_host(m.di.mem, l, tile * 16, b1)
+        got = untile_keys(m.krt[l:l + 1, tile * 16:(tile + 1) * 16], 16)[0][: b1 - tile * 16]
+        assert np.array_equal(got, rows)
+        nrm = untile_norms(m.krn[l:l + 1, tile * 16:(tile + 1) * 16], 16)[0][: b1 - tile * 16]
+        assert np.allclose(nrm, O.head_norms(rows), rtol=1e-6, atol=0)
+    qr = m.di.qr()
+    ids, sc, dsc = m.route(qr, cfg.k)
+    torch.cuda.synchronize()
+    ids_h, sc_h, dsc_h = ids.cpu().numpy(), sc.cpu().numpy(), dsc.cpu().numpy()
+    check_needles(cfg, ids_h)
+    nd = S.needle_docs(cfg)
+    # selection is exact on the GPU's own scores for every (layer, query)
+    for l in range(cfg.n_layers):
+        for b in range(cfg.B):
+            assert ids_h[l, b].tolist() == exact_topk_of(dsc_h[l, b], cfg.k).tolist(), (l, b)
+    # document scores of sampled documents against the oracle
+    for l, b in route_pairs:
+        docs = np.unique(np.concatenate([rng.integers(0, m.n_docs, n_random_docs),
+                                         nd[b] if b < nd.shape[0] else [], ids_h[l, b]]).astype(np.int64))
+        q = S.qr_host(cfg, l)[b, :cfg.T]
+        for d in docs:
+            rows = route_rows_host(m.di.mem, l, int(off[d]), int(off[d + 1]))
+            s = O.doc_scores(q, rows, np.array([0, rows.shape[0]]))[0]
+            assert abs(s - dsc_h[l, b, d]) < SCORE_TOL, (l, b, d, s, dsc_h[l, b, d])
+    ck, cv, cl = m.gather(ids)
+    q, lk, lv, ll = m.di.decode_inputs()
+    check_gather_decode(m, ids, ck, cv, cl, q, lk, lv, ll, decode_pairs)
+    return m
+
+
+def test_10m_tokens_sampled():
+    m = prepooled_case("10m", [(0, 0), (9, 31), (17, 13)], [(0, 0), (17, 31), (5, 16)], 150)
+    m.free()
+
+
+def test_100m_tokens_sampled_and_interleaved_rerouting():
+    m = prepooled_case("100m", [(0, 0), (8, 0), (17, 0)], [(0, 0), (17, 0)], 150)
+    # interleaved re-routing on the same memory: 8 queries, rounds of 64 -> 576 -> 1,088 tokens
+    cfg4 = S.CONFIGS["interleaved"]
+    print("case: interleaved re-routing, 8 queries x 3 rounds", flush=True)
+    di4 = DeviceInputs(cfg4, DEV)
+    qr = di4.qr()                                  # [L][8][1088][8][128]
+    L, B, k = cfg4.n_layers, cfg4.B, cfg4.k
+    scores = torch.empty((L, B, m.n_docs), dtype=torch.float32, device=DEV)
+    prev = None
+    lo = 0
+    nd0 = set(S.needle_docs(cfg4)[0].tolist())
+    for T in cfg4.T_rounds:
+        ids, sc, scores = m.route(qr[:, :, lo:T].contiguous(), k, doc_scores=scores, accumulate=lo > 0)
+        torch.cuda.synchronize()
+        cur = scores.clone()
+        if prev is not None:
+            assert bool((cur >= prev).all())          # a grown query never lowers a score
+        ids_h = ids.cpu().numpy()
+        for l in range(L):
+            assert nd0 <= set(ids_h[l, 0].tolist()), l    # query 0's needles stay selected
+        prev = cur
+        lo = T
+    full_ids, _, full = m.route(qr, k)
+    torch.cuda.synchronize()
+    assert torch.equal(full, prev)                    # incremental == full recompute, bit-exact
+    assert torch.equal(full_ids, ids)
+    # oracle on sampled documents of the grown queries
+    rng = np.random.default_rng(404)
+    off = m.blk.numpy()
+    dsc_h = full.cpu().numpy()
+    ids_h = full_ids.cpu().numpy()
+    for l, b in [(0, 0), (11, 5)]:
+        q = S.qr_host(cfg4, l)[b]
+        for d in np.unique(np.concatenate([rng.integers(0, m.n_docs, 12), ids_h[l, b, :4]])):
+            rows = route_rows_host(m.di.mem, l, int(off[d]), int(off[d + 1]))
+            s = O.doc_scores(q, rows, np.array([0, rows.shape[0]]))[0]
+            assert abs(s - dsc_h[l, b, d]) < SCORE_TOL, (l, b, d)
+    # decode with the grown query as the local KV
+    ck, cv, cl = m.gather(full_ids)
+    q, lk, lv, ll = di4.decode_inputs()
+    check_gather_decode(m, full_ids, ck, cv, cl, q, lk, lv, ll, [(0, 0), (17, 7)])
+    m.free()
