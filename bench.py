@@ -27,6 +27,21 @@ SCAN_BYTES_PER_BLOCK_LAYER = 2048 + 32    # bf16 Kr-bar row (8 x 128) + 8 fp32 n
 DECODE_BYTES_PER_ROW = 2 * 8 * 128 * 2    # K and V row of all 8 KV heads
 POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 
+# HBM traffic of one route-scan launch at the 100M-token workload, from the FETCH_SIZE and
+# WRITE_SIZE rocprofv3 passes (scaled by a 1 GiB calibration kernel) recorded in
+# profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
+# sources' digest differs, the figure is stale and bench.py reports null.
+SCAN_TRAFFIC_BYTES = 58.703e9
+SCAN_TRAFFIC_SOURCE_DIGEST = "1f0206a713cb3f3302bbb8c45543e1e41c7edc2640dfa238d73439c909eb83f4"
+
+
+def scan_source_digest():
+    import hashlib
+    csrc = os.path.join(ROOT, "routed_kv_memory_amd", "csrc")
+    parts = [hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
+             for f in ("route.hip", "msa_device.hpp")]
+    return hashlib.sha256("".join(parts).encode()).hexdigest()
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -36,6 +51,9 @@ def parse():
     ap.add_argument("--workload", default="100m", choices=["tiny", "1m", "10m", "100m"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run a 1 GiB fill and a 1 GiB elementwise copy (kernels of known traffic, "
+                         "used to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -182,13 +200,26 @@ def main():
         "needles_are_topk": needle_ok,
         "roofline": {"bound": "hbm", "kernel": "route_mfma_kernel (msa_route_scores)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": (round(SCAN_TRAFFIC_BYTES / 1e9, 3)
+                                 if cfg.name == "100m" and scan_source_digest() == SCAN_TRAFFIC_SOURCE_DIGEST
+                                 else None),
+                     "traffic_unit": "GB per launch", "algorithmic_GB_per_launch": round(scan_bytes / 1e9, 3)},
     }
     if cfg.per_token:
         pool_ms = float(seg_mean[0])
         result["pooled_tokens_per_s"] = round(L * n_tok / (pool_ms * 1e-3), 1)
         result["pool_GBps"] = round(L * n_tok * POOL_BYTES_PER_TOKEN / (pool_ms * 1e-3) / 1e9, 2)
 
+    if args.calibrate_copy:
+        del ck, cv
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(7)                        # writes 1 GiB
+        torch.cuda.synchronize()
+        torch.add(src, 1, out=dst)          # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = 1 << 30
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, n_blk, blk.numpy(), args.cpu_seconds)
     print(json.dumps(result), flush=True)
