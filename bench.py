@@ -23,7 +23,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routing scan GB/s (% HBM peak) + ms/query, 18 layers, 100M-token memory"
 HBM_PEAK_GBPS = 8000.0
-SCAN_BYTES_PER_BLOCK_LAYER = 2048 + 32    # bf16 Kr-bar row (8 x 128) + 8 fp32 norms
+SCAN_BYTES_PER_BLOCK_LAYER = 2048         # bf16 Kr-bar row (8 x 128): key norms are computed in-kernel
+SCAN_BYTES_PER_BLOCK = 4                   # int32 block -> document map entry, needed once per launch
+SCAN_BYTES_PER_DOC_LAYER = 4               # fp32 document score written per (layer, query)
 DECODE_BYTES_PER_ROW = 2 * 8 * 128 * 2    # K and V row of all 8 KV heads
 POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 
@@ -31,8 +33,8 @@ POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 # WRITE_SIZE rocprofv3 passes (scaled by a 1 GiB calibration kernel) recorded in
 # profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
 # sources' digest differs, the figure is stale and bench.py reports null.
-SCAN_TRAFFIC_BYTES = 58.703e9
-SCAN_TRAFFIC_SOURCE_DIGEST = "1f0206a713cb3f3302bbb8c45543e1e41c7edc2640dfa238d73439c909eb83f4"
+SCAN_TRAFFIC_BYTES = 57.694e9
+SCAN_TRAFFIC_SOURCE_DIGEST = "49d562a497da749e0e6c91c9dfc66d7cd7cabe13171c85576bd5e12bbefde6db"
 
 
 def scan_source_digest():
@@ -131,7 +133,7 @@ def main():
         if pool_args is not None:
             msa.msa_pool_blocks(*pool_args)
         rec(1)
-        msa.msa_route_scores(qr, krt, krn, n_blk, blk_doc, n_docs, dsc)
+        msa.msa_route_scores(qr, krt, n_blk, blk_doc, n_docs, dsc)
         rec(2)
         msa.msa_topk_docs(dsc, k, ids, tsc, ws_topk)
         rec(3)
@@ -161,7 +163,8 @@ def main():
     needle_ok = all(set(ids_h[l, b].tolist()) == set(nd[b].tolist())
                     for l in range(L) for b in range(nd.shape[0])) if cfg.needles == k else None
 
-    scan_bytes = L * n_blk * SCAN_BYTES_PER_BLOCK_LAYER
+    scan_bytes = (L * n_blk * SCAN_BYTES_PER_BLOCK_LAYER + n_blk * SCAN_BYTES_PER_BLOCK
+                  + L * B * n_docs * SCAN_BYTES_PER_DOC_LAYER)
     value = scan_bytes * args.steps / wall / 1e9                       # GB/s over whole steps
     scan_ms = float(seg_mean[1])
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9

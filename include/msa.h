@@ -97,7 +97,9 @@ int msa_block_offsets_host(const int64_t* doc_tok_off_host, int32_t n_docs,
  *   krbar_norm [l][tile][h][b]        = || Kr-bar[tile*16 + b][h] ||_2 (fp32; 0 for padding)
  *
  * so each 1 KiB of a tile is one matrix-core operand fragment for 16 blocks.
- * Sizes per layer: msa_route_tiles(n_blk) * 16384 bf16 and * 128 floats. */
+ * Sizes per layer: msa_route_tiles(n_blk) * 16384 bf16 and * 128 floats.  The norms
+ * are an optional output of the pooling/packing calls (the routing scan recomputes
+ * them from the keys it streams, so it reads nothing else). */
 int64_t msa_route_tiles(int64_t n_blk);
 
 /* ------------------------------------------------------------- A1: block pooling
@@ -112,7 +114,7 @@ int64_t msa_route_tiles(int64_t n_blk);
  *   doc_tok_off    [n_docs + 1] int64, device
  *   doc_blk_off    [n_docs + 1] int64, device (as msa_block_offsets_host computes)
  *   kbar, vbar     [n_layers][n_blk][8][128] bf16, row-major outputs
- *   krbar_route    route-key layout (above), output; krbar_norm its norms, output
+ *   krbar_route    route-key layout (above), output; krbar_norm its norms, output (may be NULL)
  *
  * Norms are of the rounded bf16 Kr-bar.  Errors: NULL pointers, n_layers/n_docs < 1,
  * n_tok < 0, n_blk < 0. */
@@ -123,8 +125,8 @@ int msa_pool_blocks(int32_t n_layers, const uint16_t* k, const uint16_t* v, cons
                     void* stream);
 
 /* Routing keys that already exist row-major ([n_layers][n_blk][8][128] bf16, e.g. a
- * memory bank built elsewhere) -> route-key layout + norms, as msa_pool_blocks
- * writes them.  Errors: NULL pointers, n_layers < 1, n_blk < 0. */
+ * memory bank built elsewhere) -> route-key layout + norms (krbar_norm may be NULL),
+ * as msa_pool_blocks writes them.  Errors: NULL pointers, n_layers < 1, n_blk < 0. */
 int msa_pack_route_keys(int32_t n_layers, const uint16_t* krbar_rows, int64_t n_blk,
                         uint16_t* krbar_route, float* krbar_norm, void* stream);
 
@@ -147,7 +149,7 @@ int msa_block_doc_map(const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk,
  *   doc_scores[l][b][d] = max_{t < T, n in d} s(t, n)      (-inf for a 0-block doc)
  *
  *   qr           [n_layers][B][T][8][128] bf16
- *   krbar_route, krbar_norm   route-key layout of n_blk blocks per layer
+ *   krbar_route  route-key layout of n_blk blocks per layer
  *   blk_doc      block -> document map (msa_block_doc_map) of the same memory
  *   doc_scores   [n_layers][B][n_docs] fp32, output (accumulate = 0) or in/out
  *                (accumulate = 1: the result is max(previous value, new scores),
@@ -157,7 +159,7 @@ int msa_block_doc_map(const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk,
  * Queries with T >= 16 use bf16 matrix cores (fp32 accumulate); shorter ones use
  * vector dot products.  Errors: NULL pointers, n_layers/B/T/n_docs < 1, n_blk < 0. */
 int msa_route_scores(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
-                     const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
+                     const uint16_t* krbar_route, int64_t n_blk,
                      const int32_t* blk_doc, int32_t n_docs, int32_t accumulate,
                      float* doc_scores, void* stream);
 
@@ -181,7 +183,7 @@ int msa_topk_docs(int32_t n_layers, int32_t B, const float* doc_scores, int32_t 
  * NULL; if given it receives a copy of them). */
 size_t msa_route_topk_workspace_size(int32_t n_layers, int32_t B, int32_t n_docs, int32_t k);
 int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
-                   const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
+                   const uint16_t* krbar_route, int64_t n_blk,
                    const int32_t* blk_doc, int32_t n_docs, int32_t k,
                    int32_t* topk_ids, float* topk_scores, float* doc_scores,
                    void* workspace, size_t workspace_bytes, void* stream);

@@ -117,7 +117,7 @@ MSA_API int msa_pool_blocks(int32_t n_layers, const uint16_t* k, const uint16_t*
                             int64_t n_tok, const int64_t* doc_tok_off, const int64_t* doc_blk_off, int32_t n_docs,
                             int64_t n_blk, uint16_t* kbar, uint16_t* vbar, uint16_t* krbar_route,
                             float* krbar_norm, void* stream) {
-  if (!k || !v || !kr || !doc_tok_off || !doc_blk_off || !kbar || !vbar || !krbar_route || !krbar_norm)
+  if (!k || !v || !kr || !doc_tok_off || !doc_blk_off || !kbar || !vbar || !krbar_route)
     return fail(MSA_ERR_NULL, "msa_pool_blocks: null pointer");
   if (n_layers < 1 || n_docs < 1 || n_tok < 0 || n_blk < 0)
     return fail(MSA_ERR_SHAPE, "msa_pool_blocks: n_layers=%d n_docs=%d n_tok=%lld n_blk=%lld", n_layers, n_docs,
@@ -130,7 +130,7 @@ MSA_API int msa_pool_blocks(int32_t n_layers, const uint16_t* k, const uint16_t*
 
 MSA_API int msa_pack_route_keys(int32_t n_layers, const uint16_t* krbar_rows, int64_t n_blk, uint16_t* krbar_route,
                                 float* krbar_norm, void* stream) {
-  if (!krbar_rows || !krbar_route || !krbar_norm) return fail(MSA_ERR_NULL, "msa_pack_route_keys: null pointer");
+  if (!krbar_rows || !krbar_route) return fail(MSA_ERR_NULL, "msa_pack_route_keys: null pointer");
   if (n_layers < 1 || n_blk < 0) return fail(MSA_ERR_SHAPE, "msa_pack_route_keys: n_layers=%d n_blk=%lld", n_layers,
                                              (long long)n_blk);
   if (msa::route_tiles(n_blk) > INT32_MAX) return fail(MSA_ERR_UNSUPPORTED, "msa_pack_route_keys: n_blk too large");
@@ -151,9 +151,8 @@ MSA_API int msa_block_doc_map(const int64_t* doc_blk_off, int32_t n_docs, int64_
 }
 
 static int check_route_args(const char* fn, int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
-                            const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
-                            const int32_t* blk_doc, int32_t n_docs) {
-  if (!qr || !krbar_route || !krbar_norm || !blk_doc) return fail(MSA_ERR_NULL, "%s: null pointer", fn);
+                            const uint16_t* krbar_route, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs) {
+  if (!qr || !krbar_route || !blk_doc) return fail(MSA_ERR_NULL, "%s: null pointer", fn);
   if (n_layers < 1 || B < 1 || T < 1 || n_docs < 1 || n_blk < 0)
     return fail(MSA_ERR_SHAPE, "%s: n_layers=%d B=%d T=%d n_docs=%d n_blk=%lld", fn, n_layers, B, T, n_docs,
                 (long long)n_blk);
@@ -165,12 +164,12 @@ static int check_route_args(const char* fn, int32_t n_layers, const uint16_t* qr
 }
 
 MSA_API int msa_route_scores(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T, const uint16_t* krbar_route,
-                             const float* krbar_norm, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs,
-                             int32_t accumulate, float* doc_scores, void* stream) {
-  int st = check_route_args("msa_route_scores", n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs);
+                             int64_t n_blk, const int32_t* blk_doc, int32_t n_docs, int32_t accumulate,
+                             float* doc_scores, void* stream) {
+  int st = check_route_args("msa_route_scores", n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs);
   if (st) return st;
   if (!doc_scores) return fail(MSA_ERR_NULL, "msa_route_scores: null pointer");
-  return hip_status(msa::launch_route_scores(n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs,
+  return hip_status(msa::launch_route_scores(n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs,
                                              accumulate ? 1 : 0, doc_scores, as_stream(stream)),
                     "msa_route_scores");
 }
@@ -207,10 +206,10 @@ MSA_API size_t msa_route_topk_workspace_size(int32_t n_layers, int32_t B, int32_
 }
 
 MSA_API int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T, const uint16_t* krbar_route,
-                           const float* krbar_norm, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs,
-                           int32_t k, int32_t* topk_ids, float* topk_scores, float* doc_scores, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  int st = check_route_args("msa_route_topk", n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs);
+                           int64_t n_blk, const int32_t* blk_doc, int32_t n_docs, int32_t k, int32_t* topk_ids,
+                           float* topk_scores, float* doc_scores, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  int st = check_route_args("msa_route_topk", n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs);
   if (st) return st;
   if (!topk_ids || !workspace) return fail(MSA_ERR_NULL, "msa_route_topk: null pointer");
   if (k < 1 || k > n_docs) return fail(MSA_ERR_SHAPE, "msa_route_topk: k=%d n_docs=%d", k, n_docs);
@@ -223,8 +222,7 @@ MSA_API int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int3
   float* scores = doc_scores ? doc_scores : reinterpret_cast<float*>(ws);
   char* rest = ws + align256((size_t)n_layers * B * n_docs * sizeof(float));
   hipStream_t s = as_stream(stream);
-  hipError_t e = msa::launch_route_scores(n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs, 0,
-                                          scores, s);
+  hipError_t e = msa::launch_route_scores(n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs, 0, scores, s);
   if (e != hipSuccess) return hip_status(e, "msa_route_topk (scores)");
   e = msa::launch_topk((int64_t)n_layers * B, scores, n_docs, k, topk_ids, topk_scores, rest, s);
   if (e != hipSuccess) return hip_status(e, "msa_route_topk (top-k)");

@@ -73,6 +73,32 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Sum / max over the four 16-lane rows at the same row position (lanes l, l^16,
+// l^32, l^48) with the gfx950 row-swap instructions: VALU only, no LDS crossbar.
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// DPP row shifts: lane i of each 16-lane row receives lane i + N (shl) or i - N (shr)
+// of the same row; lanes whose source falls outside the row receive `fill`.
+template <int N>
+__device__ __forceinline__ int row_shl(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, 0x100 + N, 0xF, 0xF, false);
+}
+template <int N>
+__device__ __forceinline__ int row_shr(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, 0x110 + N, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));

@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(256) pool_kernel(const uint4* __restrict__ k, 
     // route layout: [layer][tile][h][c][b][8]
     krt[((layer * tiles + tile) * kHeads + h) * (kTile * 16) + c * kTile + b] = orr;
     ss = row16_sum(ss);   // the 16 lanes of a DPP row hold the 16 chunks of head h
-    if (c == 0) krn[((layer * tiles + tile) * kHeads + h) * kTile + b] = sqrtf(ss);
+    if (krn && c == 0) krn[((layer * tiles + tile) * kHeads + h) * kTile + b] = sqrtf(ss);
   }
 }
 
@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint4* __restrict__ row
     }
     krt[((layer * tiles + tile) * kHeads + h) * (kTile * 16) + c * kTile + b] = w;
     ss = row16_sum(ss);
-    if (c == 0) krn[((layer * tiles + tile) * kHeads + h) * kTile + b] = sqrtf(ss);
+    if (krn && c == 0) krn[((layer * tiles + tile) * kHeads + h) * kTile + b] = sqrtf(ss);
   }
 }
 

@@ -37,12 +37,11 @@ _SIGS = {
     "msa_pool_blocks": ([_I32, _P, _P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "msa_pack_route_keys": ([_I32, _P, _I64, _P, _P, _P], ctypes.c_int),
     "msa_block_doc_map": ([_P, _I32, _I64, _P, _P], ctypes.c_int),
-    "msa_route_scores": ([_I32, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I32, _P, _P], ctypes.c_int),
+    "msa_route_scores": ([_I32, _P, _I32, _I32, _P, _I64, _P, _I32, _I32, _P, _P], ctypes.c_int),
     "msa_topk_docs_workspace_size": ([_I32, _I32, _I32, _I32], _SZ),
     "msa_topk_docs": ([_I32, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "msa_route_topk_workspace_size": ([_I32, _I32, _I32, _I32], _SZ),
-    "msa_route_topk": ([_I32, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
-                       ctypes.c_int),
+    "msa_route_topk": ([_I32, _P, _I32, _I32, _P, _I64, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "msa_gather_ctx": ([_I32, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _I64, _I32, _P, _P, _P, _P], ctypes.c_int),
     "msa_sparse_decode_workspace_size": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_decode": ([_I32, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _F32, _P, _P, _SZ, _P],
@@ -142,21 +141,22 @@ def msa_route_tiles(n_blk: int) -> int:
 
 # ----------------------------------------------------------------------- entry points
 
-def msa_pool_blocks(k, v, kr, doc_tok_off, doc_blk_off, n_blk, kbar, vbar, krbar_route, krbar_norm, stream=None):
+def msa_pool_blocks(k, v, kr, doc_tok_off, doc_blk_off, n_blk, kbar, vbar, krbar_route, krbar_norm=None,
+                    stream=None):
     L, n_tok = k.shape[0], k.shape[1]
     n_docs = doc_tok_off.numel() - 1
     _check("msa_pool_blocks", lib().msa_pool_blocks(
         L, _ptr(k, _BF16, "k"), _ptr(v, _BF16, "v"), _ptr(kr, _BF16, "kr"), n_tok,
         _ptr(doc_tok_off, _I64T, "doc_tok_off"), _ptr(doc_blk_off, _I64T, "doc_blk_off"), n_docs, n_blk,
         _ptr(kbar, _BF16, "kbar"), _ptr(vbar, _BF16, "vbar"), _ptr(krbar_route, _BF16, "krbar_route"),
-        _ptr(krbar_norm, _F32T, "krbar_norm"), _stream(stream)))
+        _ptr(krbar_norm, _F32T, "krbar_norm", allow_none=True), _stream(stream)))
 
 
-def msa_pack_route_keys(krbar_rows, n_blk, krbar_route, krbar_norm, stream=None):
+def msa_pack_route_keys(krbar_rows, n_blk, krbar_route, krbar_norm=None, stream=None):
     L = krbar_rows.shape[0]
     _check("msa_pack_route_keys", lib().msa_pack_route_keys(
         L, _ptr(krbar_rows, _BF16, "krbar_rows"), n_blk, _ptr(krbar_route, _BF16, "krbar_route"),
-        _ptr(krbar_norm, _F32T, "krbar_norm"), _stream(stream)))
+        _ptr(krbar_norm, _F32T, "krbar_norm", allow_none=True), _stream(stream)))
 
 
 def msa_block_doc_map(doc_blk_off, n_blk, blk_doc, stream=None):
@@ -165,12 +165,11 @@ def msa_block_doc_map(doc_blk_off, n_blk, blk_doc, stream=None):
         _ptr(doc_blk_off, _I64T, "doc_blk_off"), n_docs, n_blk, _ptr(blk_doc, _I32T, "blk_doc"), _stream(stream)))
 
 
-def msa_route_scores(qr, krbar_route, krbar_norm, n_blk, blk_doc, n_docs, doc_scores, accumulate=False,
-                     stream=None):
+def msa_route_scores(qr, krbar_route, n_blk, blk_doc, n_docs, doc_scores, accumulate=False, stream=None):
     L, B, T = qr.shape[0], qr.shape[1], qr.shape[2]
     _check("msa_route_scores", lib().msa_route_scores(
         L, _ptr(qr, _BF16, "qr"), B, T, _ptr(krbar_route, _BF16, "krbar_route"),
-        _ptr(krbar_norm, _F32T, "krbar_norm"), n_blk, _ptr(blk_doc, _I32T, "blk_doc"), n_docs,
+        n_blk, _ptr(blk_doc, _I32T, "blk_doc"), n_docs,
         1 if accumulate else 0, _ptr(doc_scores, _F32T, "doc_scores"), _stream(stream)))
 
 
@@ -190,12 +189,12 @@ def msa_route_topk_workspace_size(n_layers, B, n_docs, k) -> int:
     return int(lib().msa_route_topk_workspace_size(n_layers, B, n_docs, k))
 
 
-def msa_route_topk(qr, krbar_route, krbar_norm, n_blk, blk_doc, n_docs, k, topk_ids, topk_scores, workspace,
-                   doc_scores=None, stream=None):
+def msa_route_topk(qr, krbar_route, n_blk, blk_doc, n_docs, k, topk_ids, topk_scores, workspace, doc_scores=None,
+                   stream=None):
     L, B, T = qr.shape[0], qr.shape[1], qr.shape[2]
     _check("msa_route_topk", lib().msa_route_topk(
         L, _ptr(qr, _BF16, "qr"), B, T, _ptr(krbar_route, _BF16, "krbar_route"),
-        _ptr(krbar_norm, _F32T, "krbar_norm"), n_blk, _ptr(blk_doc, _I32T, "blk_doc"), n_docs, k,
+        n_blk, _ptr(blk_doc, _I32T, "blk_doc"), n_docs, k,
         _ptr(topk_ids, _I32T, "topk_ids"), _ptr(topk_scores, _F32T, "topk_scores", allow_none=True),
         _ptr(doc_scores, _F32T, "doc_scores", allow_none=True), _ptr(workspace, _ANY, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -65,7 +65,7 @@ def route(qr, krt, krn, n_blk, blk_off_d, k, dev="cuda", blk_doc=None):
     ids = torch.empty((L, B, k), dtype=torch.int32, device=dev)
     sc = torch.empty((L, B, k), dtype=torch.float32, device=dev)
     dsc = torch.empty((L, B, n_docs), dtype=torch.float32, device=dev)
-    msa.msa_route_topk(qr, krt, krn, n_blk, blk_doc, n_docs, k, ids, sc, ws, doc_scores=dsc)
+    msa.msa_route_topk(qr, krt, n_blk, blk_doc, n_docs, k, ids, sc, ws, doc_scores=dsc)
     return ids, sc, dsc
 
 

@@ -93,7 +93,7 @@ class Memory:
         L, B = qr.shape[0], qr.shape[1]
         if doc_scores is None:
             doc_scores = torch.empty((L, B, self.n_docs), dtype=torch.float32, device=DEV)
-        msa.msa_route_scores(qr, self.krt, self.krn, self.n_blk, self.blk_doc, self.n_docs, doc_scores,
+        msa.msa_route_scores(qr, self.krt, self.n_blk, self.blk_doc, self.n_docs, doc_scores,
                              accumulate=accumulate)
         ids = torch.empty((L, B, k), dtype=torch.int32, device=DEV)
         sc = torch.empty((L, B, k), dtype=torch.float32, device=DEV)

@@ -137,11 +137,11 @@ def test_route_accumulate_equals_full_query():
     n_docs = len(off) - 1
     m = doc_map(blk_d, n_blk)
     full = torch.empty((L, B, n_docs), dtype=torch.float32, device=DEV)
-    msa.msa_route_scores(to_dev_bf16(qr), krt, krn, n_blk, m, n_docs, full)
+    msa.msa_route_scores(to_dev_bf16(qr), krt, n_blk, m, n_docs, full)
     inc = torch.empty_like(full)
-    msa.msa_route_scores(to_dev_bf16(qr[:, :, :64]), krt, krn, n_blk, m, n_docs, inc)
+    msa.msa_route_scores(to_dev_bf16(qr[:, :, :64]), krt, n_blk, m, n_docs, inc)
     first = inc.clone()
-    msa.msa_route_scores(to_dev_bf16(qr[:, :, 64:]), krt, krn, n_blk, m, n_docs, inc, accumulate=True)
+    msa.msa_route_scores(to_dev_bf16(qr[:, :, 64:]), krt, n_blk, m, n_docs, inc, accumulate=True)
     torch.cuda.synchronize()
     assert torch.equal(inc, full)
     assert bool((inc >= first).all())
