@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routing scan GB/s (% HBM peak) + ms/query, 18 layers, 100M-token memory"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0             # dense bf16 matrix-core peak
 SCAN_BYTES_PER_BLOCK_LAYER = 2048         # bf16 Kr-bar row (8 x 128): key norms are computed in-kernel
 SCAN_BYTES_PER_BLOCK = 4                   # int32 block -> document map entry, needed once per launch
 SCAN_BYTES_PER_DOC_LAYER = 4               # fp32 document score written per (layer, query)
@@ -33,8 +34,8 @@ POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 # WRITE_SIZE rocprofv3 passes (scaled by a 1 GiB calibration kernel) recorded in
 # profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
 # sources' digest differs, the figure is stale and bench.py reports null.
-SCAN_TRAFFIC_BYTES = 57.694e9
-SCAN_TRAFFIC_SOURCE_DIGEST = "49d562a497da749e0e6c91c9dfc66d7cd7cabe13171c85576bd5e12bbefde6db"
+SCAN_TRAFFIC_BYTES = 57.690e9
+SCAN_TRAFFIC_SOURCE_DIGEST = "f1f82a81ea3fbae1d31cdbe0363ea523cc920825be6a3d9eb1fa3f27436201b3"
 
 
 def scan_source_digest():
@@ -168,6 +169,23 @@ def main():
     value = scan_bytes * args.steps / wall / 1e9                       # GB/s over whole steps
     scan_ms = float(seg_mean[1])
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    # The scan does 2*B*T*1024 flop per 2,048-byte key row: below the ridge (peak flop/s over
+    # peak B/s, ~312 flop/B) it is bound by HBM, above it by the matrix cores.
+    scan_flop = 2.0 * B * T * 1024 * L * n_blk
+    if scan_flop / scan_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        tflops = scan_flop / (scan_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "route_mfma_kernel (msa_route_scores)",
+                    "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "algorithmic_flop_per_launch": scan_flop, "hbm_GBps": round(achieved, 2)}
+    else:
+        roofline = {"bound": "hbm", "kernel": "route_mfma_kernel (msa_route_scores)",
+                    "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": (round(SCAN_TRAFFIC_BYTES / 1e9, 3)
+                                if cfg.name == "100m" and scan_source_digest() == SCAN_TRAFFIC_SOURCE_DIGEST
+                                else None),
+                    "traffic_unit": "GB per launch", "algorithmic_GB_per_launch": round(scan_bytes / 1e9, 3)}
     ctx_rows = int(cl.sum().item())
     dec_rows = ctx_rows + int(ll.sum().item())
     result = {
@@ -201,13 +219,7 @@ def main():
         "decode_us_per_token": round(float(seg_mean[4]) * 1e3, 2),
         "decode_rows": dec_rows,
         "needles_are_topk": needle_ok,
-        "roofline": {"bound": "hbm", "kernel": "route_mfma_kernel (msa_route_scores)",
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": (round(SCAN_TRAFFIC_BYTES / 1e9, 3)
-                                 if cfg.name == "100m" and scan_source_digest() == SCAN_TRAFFIC_SOURCE_DIGEST
-                                 else None),
-                     "traffic_unit": "GB per launch", "algorithmic_GB_per_launch": round(scan_bytes / 1e9, 3)},
+        "roofline": roofline,
     }
     if cfg.per_token:
         pool_ms = float(seg_mean[0])

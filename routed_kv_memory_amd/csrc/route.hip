@@ -11,17 +11,19 @@
 //  * Queries of >= 16 tokens: per KV head the scan is a [tokens x 128] . [128 x
 //    blocks] bf16 contraction on v_mfma_f32_16x16x32_bf16.  The route-key tile
 //    layout makes each head's slice of a 16-block tile four contiguous 1 KiB MFMA
-//    fragments, so keys go from HBM straight into registers; the query chunk stays
-//    in registers for the whole layer.  The per-head cosine scaling 1/(|q| |k|) is
+//    fragments, so keys go from HBM straight into registers; the query chunk is
+//    staged in LDS once per layer.  The per-head cosine scaling 1/(|q| |k|) is
 //    applied to the fp32 accumulators, so the bf16 inputs enter the matrix cores
-//    exactly as stored; key norms are summed from the fragments already held, so
-//    the scan reads nothing but the keys and the block -> document map.
+//    exactly as stored; key norms come from the same fragments (the diagonal of
+//    K K^T on the matrix cores), so the scan reads nothing but the keys and the
+//    block -> document map.
 //  * Persistent grid over all CUs: each 512-thread workgroup owns a contiguous
-//    range of (layer, tile) items for one 64-token query chunk; ranges sharing a
-//    chunk are placed XCD by XCD.
-//  * Heads meet in LDS once per two tiles; the max over tokens is a cross-lane
-//    reduction; the per-document max is a segmented scan keyed by a block ->
-//    document map, with each document emitted once per range.
+//    range of (layer, tile) items for one 64-token query chunk (the chunks that
+//    share a range are placed on one XCD); per layer it stages the chunk's query
+//    in LDS and each wave then scans its own contiguous share of the range.
+//  * A wave walks the 8 heads of a tile itself, so the head sum, the max over
+//    tokens and the per-document max (a segmented scan keyed by a block ->
+//    document map, each document emitted once) all stay in registers.
 //  * Queries of < 16 tokens use a vector-ALU kernel over the same layout.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
@@ -79,30 +81,34 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 
 // ---------------------------------------------------------------- MFMA scan
 //
-// One workgroup per CU, 8 waves: wave h owns KV head h.  It keeps the query
-// chunk's head-h fragments (64 tokens x 128 dims) in registers for the whole
-// layer, and streams only its own head's 4 KiB of each 16-block route tile (four
-// contiguous 1 KiB fragments) through a register ring, four tiles ahead, with
-// nontemporal loads.  The same fragment bytes serve as the A operand (query:
-// rows = tokens) and the B operand (keys: columns = blocks) of
+// One workgroup per CU, 8 waves.  The workgroup owns a contiguous range of
+// (layer, tile) items for one 64-token query chunk and walks it layer by layer:
+// per layer the 8 waves stage the chunk's query fragments (64 tokens x 8 heads x
+// 128 dims, 128 KiB) and inverse norms in LDS, then each wave scans its own
+// contiguous eighth of the layer's items with no further synchronisation.
+//
+// Per tile a wave streams the 8 heads' 4 KiB key slices (four contiguous 1 KiB
+// fragments each) through a register ring, three slices ahead, with nontemporal
+// loads.  The same fragment bytes serve as the A operand (query: rows = tokens,
+// read from LDS) and the B operand (keys: columns = blocks) of
 // v_mfma_f32_16x16x32_bf16, so lane l ends up owning block (l & 15) and tokens
-// 4*(l >> 4) + r: the key norm is summed from the fragment the lane already holds,
-// and the per-head cosine scaling 1/(|q| |k|) is applied to the fp32 accumulators
-// before the head sum.  The 8 heads' scaled partials of two consecutive tiles
-// meet in LDS behind one barrier (double buffered, so the next two tiles' matrix
-// work overlaps the reduction); waves 4..7 sum them for one token group each and
-// take the max over its 16 tokens; wave 0 folds the token groups and keeps each
-// document's running maximum across tiles, emitting it once when the document
-// ends (a plain store when no other workgroup can touch that document, an atomic
-// max otherwise).
-constexpr int kScanWaves = kHeads;              // one wave per KV head
+// 4*(l >> 4) + r of each 16-token group.  Per head four more MFMAs of the key
+// fragments with themselves give K K^T, whose diagonal is the blocks' squared
+// norms; the fp32 accumulators are scaled by 1/(|q| |k|) and added into the
+// lane's running head sum, all in registers.
+// After the 8th head the lane takes the max over its tokens, a cross-lane max
+// completes it over the 64 tokens, and the block maxima are folded into
+// per-document maxima: a segmented scan over the 16 blocks, with each document's
+// running maximum carried across the wave's consecutive tiles and emitted once
+// when the document ends (a plain store when no other wave or workgroup can touch
+// that document, an atomic max otherwise).
+constexpr int kScanWaves = 8;
 constexpr int kScanWG = kScanWaves * 64;
-constexpr int kGroup = 2;                        // tiles per barrier
-constexpr int kStages = 6;                       // prefetch ring (a multiple of kGroup)
-constexpr int kAhead = 4;                        // tiles in flight per wave beyond the current one
+constexpr int kRing = 4;          // key slices (one head of one tile) held in registers; divides kHeads
+constexpr int kAhead = 3;         // slices in flight beyond the current one
 
 __device__ __forceinline__ void lds_barrier() {
-  // orders LDS only: in-flight global prefetches stay in flight across the barrier
+  // orders LDS only: in-flight global loads stay in flight across the barrier
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -118,9 +124,8 @@ __device__ __forceinline__ float sumsq8(u32x4 w) {
   return s;
 }
 
-// Document score emission: `exclusive` means this workgroup is the only writer of
-// the codes row and the codes started from zero, so a document seen whole here can
-// be stored; documents that may continue in another workgroup use atomic max.
+// Document score emission: a document that only this wave can see, in a codes row
+// that started from zero, is stored; any other goes through an atomic max.
 __device__ __forceinline__ void emit_doc(uint32_t* __restrict__ codes, int32_t doc, float v, bool atomic) {
   if (atomic) atomicMax(codes + doc, ordered_code(v));
   else codes[doc] = ordered_code(v);
@@ -131,9 +136,7 @@ __global__ void __launch_bounds__(kScanWG)
 route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t n_tc,
                   const uint4* __restrict__ krt, int64_t tiles, const int32_t* __restrict__ blk_doc,
                   int32_t n_docs, int32_t L, int32_t R, int32_t exclusive, uint32_t* __restrict__ codes) {
-  // per-head scaled partial scores of one group of tiles, double buffered
-  __shared__ float4 P[2][kGroup][kScanWaves][NT][64];
-  __shared__ float M[2][kGroup][4][kTile];       // block maxima per token group
+  __shared__ u32x4 QS[kHeads][4][NT][64];      // query fragments [head][k step][token group][lane]
   __shared__ float RQ[kHeads][kTokChunk];        // 1/max(|q|, eps) per head and token of the chunk
 
   // XCD-aware placement: workgroups are dispatched round-robin over 8 XCDs; when the
@@ -159,218 +162,195 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
   const int64_t it_end = W * (r + 1) / R;
   if (it_begin >= it_end) return;                // uniform across the workgroup
 
-  const int wave = threadIdx.x >> 6;             // = head
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int j = lane & 15;
   const float ninf = -__builtin_huge_valf();
 
-  bf16x8 q[4][NT];       // A fragments [s][nt]: token 16 nt + j, dims 32 s + 8 g .. +7
-  int cur_layer = -1;
-
-  // Prefetch cursor.  Items are consecutive, so the head's fragments of item i sit
-  // at a linear offset; loads are unconditional (past the range end the last item
-  // is fetched again) so that every wait is an exact count.
-  const uint4* isrc = krt + it_begin * kTileU4 + wave * kHeadU4 + lane;
-  int64_t itau = it_begin % tiles;
-  int64_t inext = it_begin;
-
-  u32x4 kb[kStages][4];
-  int32_t db[kStages];
-
-  // The route keys are read exactly once: nontemporal loads keep them from
-  // displacing useful lines in the caches.
-  auto issue = [&](u32x4 (&kbuf)[4], int32_t& dbuf) {
+  // accumulator row (nt, r) of this lane is token t_base + 16 nt + 4 g + r
+  uint32_t tmask = 0;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kbuf[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(isrc + s * 64));
-    dbuf = blk_doc[itau * kTile + j];
-    if (inext + 1 < it_end) {
-      ++inext;
-      isrc += kTileU4;
-      itau = (itau + 1 == tiles) ? 0 : itau + 1;
-    }
-  };
-
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-  for (int x = 0; x < kAhead; ++x) issue(kb[x], db[x]);
+    for (int rr = 0; rr < 4; ++rr)
+      if (t_base + nt * 16 + 4 * g + rr < T) tmask |= 1u << (nt * 4 + rr);
 
-  // compute cursor and wave 0's open document (the last run of the previous tile)
-  int layer = (int)(it_begin / tiles);
-  int64_t ctau = it_begin - (int64_t)layer * tiles;
-  int32_t cdoc = -1;
-  float cmax = ninf;
-  bool cshared = true;          // the open document may have blocks outside this range
-  bool seg_first = true;        // first tile of this layer inside the range
-  int pb = 0;                   // LDS buffer parity, alternates every group
-  // the tiles of the current group (c_*) and of the group wave 0 folds next (p_*)
-  bool c_valid[kGroup], c_first[kGroup], c_last[kGroup];
-  int c_layer[kGroup];
-  int32_t c_doc[kGroup];
-  bool p_valid[kGroup], p_first[kGroup], p_last[kGroup];
-  int p_layer[kGroup];
-  int32_t p_doc[kGroup];
-#pragma unroll
-  for (int u = 0; u < kGroup; ++u) p_valid[u] = false;
+  for (int64_t seg = it_begin; seg < it_end;) {
+    const int layer = (int)(seg / tiles);
+    const int64_t layer0 = (int64_t)layer * tiles;
+    const int64_t seg_end = it_end < layer0 + tiles ? it_end : layer0 + tiles;
 
-  // Wave 0: fold the block maxima of one tile (written before the last barrier)
-  // into document scores.  Blocks of a document are contiguous, so a segmented
-  // suffix max within each run of equal documents gives the run maxima; the last
-  // run stays open because the document may continue in the next tile.
-  auto flush_tile = [&](const float (&Mt)[4][kTile], bool t_first, bool t_last, int t_layer, int32_t t_doc) {
-    float v = ninf;
-    int32_t d = -1;
-    if (lane < kTile) {
-#pragma unroll
-      for (int n = 0; n < NT; ++n) v = fmaxf(v, Mt[n][lane]);
-      d = t_doc;
-      if (d >= n_docs) d = -1;   // map entries are trusted only inside [0, n_docs)
-    }
-    uint32_t* lcodes = codes + ((int64_t)t_layer * B + b) * n_docs;
-    const int32_t d0 = __builtin_amdgcn_readlane(d, 0);
-    if (cdoc >= 0 && cdoc != d0) {          // this tile does not continue the open document
-      if (lane == 0) emit_doc(lcodes, cdoc, cmax, cshared || !exclusive);
-      cdoc = -1;
-    }
-    bool run0_shared = t_first;
-    if (cdoc >= 0) {                        // lane 0's run continues the open document
-      if (lane == 0) v = fmaxf(v, cmax);
-      run0_shared = cshared;
-    }
+    lds_barrier();   // every wave is done with the previous layer's query
     {
-      const int ninf_bits = __float_as_int(ninf);
-      float vo = __int_as_float(row_shl<1>(__float_as_int(v), ninf_bits));
-      int32_t dn = row_shl<1>(d, -2);
-      if (dn == d) v = fmaxf(v, vo);
-      vo = __int_as_float(row_shl<2>(__float_as_int(v), ninf_bits));
-      dn = row_shl<2>(d, -2);
-      if (dn == d) v = fmaxf(v, vo);
-      vo = __int_as_float(row_shl<4>(__float_as_int(v), ninf_bits));
-      dn = row_shl<4>(d, -2);
-      if (dn == d) v = fmaxf(v, vo);
-      vo = __int_as_float(row_shl<8>(__float_as_int(v), ninf_bits));
-      dn = row_shl<8>(d, -2);
-      if (dn == d) v = fmaxf(v, vo);
-    }
-    const int32_t dprev = row_shr<1>(d, -2);
-    const bool head = lane < kTile && (lane == 0 || dprev != d);
-    const uint64_t heads = __ballot(head);
-    const int hl = 63 - __builtin_clzll(heads);          // head lane of the last run
-    const int32_t dl = __builtin_amdgcn_readlane(d, hl);
-    const float vl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), hl));
-    if (head && lane != hl && d >= 0) emit_doc(lcodes, d, v, (lane == 0 ? run0_shared : false) || !exclusive);
-    cdoc = dl;
-    cmax = vl;
-    cshared = hl == 0 ? run0_shared : false;
-    if (t_last) {                           // the range or the layer ends here
-      if (cdoc >= 0 && lane == 0) emit_doc(lcodes, cdoc, cmax, true);
-      cdoc = -1;
-    }
-  };
-
-  for (int64_t base = it_begin; base < it_end; base += kStages) {
+      // wave h stages head h of this layer's query chunk and its inverse norms
+      const uint16_t* qb = qr + (((int64_t)layer * B + b) * T) * kRow + wave * kDim + g * 8;
 #pragma unroll
-    for (int x = 0; x < kStages; ++x) {
-      const int64_t it = base + x;
-      const int u = x % kGroup;               // position in the group
-      issue(kb[(x + kAhead) % kStages], db[(x + kAhead) % kStages]);
-      c_valid[u] = it < it_end;               // uniform across the workgroup
-      if (c_valid[u]) {
-        if (layer != cur_layer) {
-          // this layer's query chunk, head `wave`, as fragments; inverse norms per token
-          const uint16_t* qb = qr + (((int64_t)layer * B + b) * T) * kRow + wave * kDim + g * 8;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const int tok = t_base + nt * 16 + j;
-            float ss = 0.f;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              u32x4 v = {0u, 0u, 0u, 0u};
-              if (tok < T) v = *reinterpret_cast<const u32x4*>(qb + (int64_t)tok * kRow + s * 32);
-              q[s][nt] = __builtin_bit_cast(bf16x8, v);
-              ss += sumsq8(v);
-            }
-            ss = rows4_sum(ss);
-            if (g == 0) RQ[wave][nt * 16 + j] = 1.0f / fmaxf(sqrtf(ss), kNormEps);
-          }
-          cur_layer = layer;
-        }
-
-        // C[token][block] = Q . K^T for this head; lane: block j, tokens 4 g + r
-        f32x4 acc[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float ssk = 0.f;
+      for (int nt = 0; nt < NT; ++nt) {
+        const int tok = t_base + nt * 16 + j;
+        float ss = 0.f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const bf16x8 kf = __builtin_bit_cast(bf16x8, kb[x % kStages][s]);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[s][nt], kf, acc[nt], 0, 0, 0);
-          ssk += sumsq8(kb[x % kStages][s]);
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (tok < T) v = *reinterpret_cast<const u32x4*>(qb + (int64_t)tok * kRow + s * 32);
+          QS[wave][s][nt][lane] = v;
+          ss += sumsq8(v);
         }
-        ssk = rows4_sum(ssk);
-        const float rk = __builtin_amdgcn_rcpf(fmaxf(sqrtf(ssk), kNormEps));   // block j, head `wave`
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const float4 rq = *reinterpret_cast<const float4*>(&RQ[wave][nt * 16 + 4 * g]);   // tokens 4 g + r
-          P[pb][u][wave][nt][lane] = make_float4(acc[nt][0] * (rq.x * rk), acc[nt][1] * (rq.y * rk),
-                                                 acc[nt][2] * (rq.z * rk), acc[nt][3] * (rq.w * rk));
-        }
-        const bool seg_last = (ctau + 1 == tiles) || (it + 1 == it_end);
-        c_first[u] = seg_first;
-        c_last[u] = seg_last;
-        c_layer[u] = layer;
-        c_doc[u] = db[x % kStages];
-        seg_first = seg_last;
-        if (++ctau == tiles) { ctau = 0; ++layer; }
-      }
-
-      if (u == kGroup - 1) {
-        lds_barrier();   // the only barrier per group: P[pb] complete, M[pb ^ 1] complete
-        if (wave >= kScanWaves - 4 && wave - (kScanWaves - 4) < NT) {
-          // token group n = wave - 4: sum the 8 heads, max over the group's 16 valid tokens
-          const int n = wave - (kScanWaves - 4);
-          const int tok0 = t_base + n * 16 + 4 * g;
-#pragma unroll
-          for (int v = 0; v < kGroup; ++v) {
-            if (!c_valid[v]) break;
-            float4 tot = P[pb][v][0][n][lane];
-#pragma unroll
-            for (int h = 1; h < kHeads; ++h) {
-              const float4 w = P[pb][v][h][n][lane];
-              tot.x += w.x; tot.y += w.y; tot.z += w.z; tot.w += w.w;
-            }
-            float m = tok0 < T ? tot.x : ninf;
-            m = fmaxf(m, tok0 + 1 < T ? tot.y : ninf);
-            m = fmaxf(m, tok0 + 2 < T ? tot.z : ninf);
-            m = fmaxf(m, tok0 + 3 < T ? tot.w : ninf);
-            m = rows4_max(m);
-            if (g == 0) M[pb][v][n][j] = m * 0.125f;   // head mean
-          }
-        }
-        if (wave == 0) {
-#pragma unroll
-          for (int v = 0; v < kGroup; ++v)
-            if (p_valid[v]) flush_tile(M[pb ^ 1][v], p_first[v], p_last[v], p_layer[v], p_doc[v]);
-        }
-#pragma unroll
-        for (int v = 0; v < kGroup; ++v) {
-          p_valid[v] = c_valid[v];
-          p_first[v] = c_first[v];
-          p_last[v] = c_last[v];
-          p_layer[v] = c_layer[v];
-          p_doc[v] = c_doc[v];
-        }
-        pb ^= 1;
-        if (it + 1 >= it_end) break;   // uniform across the workgroup
+        ss = rows4_sum(ss);
+        if (g == 0) RQ[wave][nt * 16 + j] = 1.0f / fmaxf(sqrtf(ss), kNormEps);
       }
     }
-  }
-  lds_barrier();        // M of the last group complete
-  if (wave == 0) {
+    lds_barrier();
+
+    // this wave's contiguous share of the layer's items
+    const int64_t n_items = seg_end - seg;
+    const int64_t w0 = seg + n_items * wave / kScanWaves;
+    const int64_t w1 = seg + n_items * (wave + 1) / kScanWaves;
+    if (w0 < w1) {
+      uint32_t* lcodes = codes + ((int64_t)layer * B + b) * n_docs;
+      const int64_t n_units = (w1 - w0) * kHeads;   // key slices of the run, consecutive in memory
+      const uint4* src = krt + w0 * kTileU4 + lane;
+      int64_t unext = 0;
+      u32x4 kb[kRing][4];
+      // Loads are unconditional (past the run's end the last slice is fetched again)
+      // so that every wait is an exact count.
+      auto issue = [&](u32x4 (&kbuf)[4]) {
 #pragma unroll
-    for (int v = 0; v < kGroup; ++v)
-      if (p_valid[v]) flush_tile(M[pb ^ 1][v], p_first[v], p_last[v], p_layer[v], p_doc[v]);
+        for (int s = 0; s < 4; ++s)
+          kbuf[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + s * 64));
+        if (unext + 1 < n_units) {
+          ++unext;
+          src += kHeadU4;
+        }
+      };
+#pragma unroll
+      for (int x = 0; x < kAhead; ++x) {
+        issue(kb[x]);
+        __builtin_amdgcn_sched_barrier(0);   // keep the ring's issue order (exact wait counts)
+      }
+
+      // open document: the last run of the previous tile
+      int32_t cdoc = -1;
+      float cmax = ninf;
+      bool cshared = true;
+      int64_t tau = w0 - layer0;                  // tile index within the layer
+      int32_t dcur = -1;
+      f32x4 tot[NT];
+
+      for (int64_t ti = w0; ti < w1; ++ti) {
+#pragma unroll
+        for (int h = 0; h < kHeads; ++h) {
+          // keeps each head's query-fragment reads from being hoisted into earlier heads
+          __builtin_amdgcn_sched_barrier(0);
+          issue(kb[(h + kAhead) % kRing]);
+          if (h == 0) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) tot[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dcur = blk_doc[tau * kTile + j];     // consumed after the 8th head
+          }
+
+          // C[token][block] = Q . K^T for head h; lane: block j, tokens 4 g + r
+          f32x4 acc[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 kk = {0.f, 0.f, 0.f, 0.f};   // K . K^T of the tile's 16 blocks for head h
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, kb[h % kRing][s]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, QS[h][s][nt][lane]), kf,
+                                                                acc[nt], 0, 0, 0);
+            kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, kf, kk, 0, 0, 0);
+          }
+          // |k_j|^2 is the diagonal entry (j, j): row j = 4 g + r sits in lane group
+          // g = j >> 2, register r = j & 3; the sum over the 4 lane groups hands it
+          // to every lane of block j.
+          const int jr = j & 3;
+          const float k01 = (jr & 1) ? kk[1] : kk[0];
+          const float k23 = (jr & 1) ? kk[3] : kk[2];
+          float ssk = (jr & 2) ? k23 : k01;
+          ssk = rows4_sum(g == (j >> 2) ? ssk : 0.f);
+          // 1/max(|k|, eps) = rsq(max(|k|^2, eps^2))
+          const float rk = __builtin_amdgcn_rsqf(fmaxf(ssk, kNormEps * kNormEps));   // block j, head h
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const float4 rq = *reinterpret_cast<const float4*>(&RQ[h][nt * 16 + 4 * g]);   // tokens 4 g + r
+            tot[nt][0] += acc[nt][0] * (rq.x * rk);
+            tot[nt][1] += acc[nt][1] * (rq.y * rk);
+            tot[nt][2] += acc[nt][2] * (rq.z * rk);
+            tot[nt][3] += acc[nt][3] * (rq.w * rk);
+          }
+
+          if (h == kHeads - 1) {
+            // block j's max over the chunk's valid tokens, as a head mean
+            float v = ninf;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr)
+                if (tmask & (1u << (nt * 4 + rr))) v = fmaxf(v, tot[nt][rr]);
+            v = rows4_max(v) * 0.125f;
+
+            // Fold the tile's 16 block maxima into document maxima.  Blocks of a
+            // document are contiguous, so a segmented suffix max within each run
+            // of equal documents gives the run maxima; the last run stays open
+            // because the document may continue in the next tile.
+            const bool t_first = tau == w0 - layer0;
+            const bool t_last = tau + 1 == w1 - layer0;
+            int32_t d = -1;
+            if (lane < kTile) {
+              d = dcur;
+              if (d >= n_docs) d = -1;   // map entries are trusted only inside [0, n_docs)
+            } else {
+              v = ninf;
+            }
+            const int32_t d0 = __builtin_amdgcn_readlane(d, 0);
+            if (cdoc >= 0 && cdoc != d0) {      // this tile does not continue the open document
+              if (lane == 0) emit_doc(lcodes, cdoc, cmax, cshared || !exclusive);
+              cdoc = -1;
+            }
+            bool run0_shared = t_first;
+            if (cdoc >= 0) {                    // lane 0's run continues the open document
+              if (lane == 0) v = fmaxf(v, cmax);
+              run0_shared = cshared;
+            }
+            {
+              const int ninf_bits = __float_as_int(ninf);
+              float vo = __int_as_float(row_shl<1>(__float_as_int(v), ninf_bits));
+              int32_t dn = row_shl<1>(d, -2);
+              if (dn == d) v = fmaxf(v, vo);
+              vo = __int_as_float(row_shl<2>(__float_as_int(v), ninf_bits));
+              dn = row_shl<2>(d, -2);
+              if (dn == d) v = fmaxf(v, vo);
+              vo = __int_as_float(row_shl<4>(__float_as_int(v), ninf_bits));
+              dn = row_shl<4>(d, -2);
+              if (dn == d) v = fmaxf(v, vo);
+              vo = __int_as_float(row_shl<8>(__float_as_int(v), ninf_bits));
+              dn = row_shl<8>(d, -2);
+              if (dn == d) v = fmaxf(v, vo);
+            }
+            const int32_t dprev = row_shr<1>(d, -2);
+            const bool head = lane < kTile && (lane == 0 || dprev != d);
+            const uint64_t heads = __ballot(head);
+            const int hl = 63 - __builtin_clzll(heads);      // head lane of the last run
+            const int32_t dl = __builtin_amdgcn_readlane(d, hl);
+            const float vl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), hl));
+            if (head && lane != hl && d >= 0)
+              emit_doc(lcodes, d, v, (lane == 0 ? run0_shared : false) || !exclusive);
+            cdoc = dl;
+            cmax = vl;
+            cshared = hl == 0 ? run0_shared : false;
+            if (t_last) {                       // the run ends here
+              if (cdoc >= 0 && lane == 0) emit_doc(lcodes, cdoc, cmax, true);
+              cdoc = -1;
+            }
+            ++tau;
+          }
+        }
+      }
+    }
+    seg = seg_end;
   }
 }
 
