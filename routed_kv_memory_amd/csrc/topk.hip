@@ -7,10 +7,15 @@
 // "MSA paper reading", 方法拆解).
 //
 // Each (score, id) becomes one 64-bit key (order-preserving score code << 32 |
-// ~id) so a single unsigned comparison realises the total order.  Pass 1: every
-// workgroup bitonic-sorts 2048 keys in LDS and keeps its k best; further passes
-// merge the candidates the same way until one workgroup per row remains, which
-// writes ids and scores.
+// ~id) so a single unsigned comparison realises the total order.  Every pass
+// splits each row into chunks, one workgroup per chunk keeps the chunk's k best
+// keys, and the next pass merges the candidates until one workgroup per row
+// remains, which writes ids and scores.
+//
+// For k <= 64 a chunk is 2048 keys held in registers (8 per lane): each wave
+// extracts its k best by repeated wave-wide maxima (DPP and row swaps, no LDS),
+// and one wave merges the four waves' lists the same way.  Larger k bitonic-sorts
+// the chunk in LDS.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -69,6 +74,108 @@ topk_pass_kernel(const float* __restrict__ scores, const uint64_t* __restrict__ 
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// ------------------------------------------------------------ register selection (k <= 64)
+
+constexpr int kSelE = 8;                        // keys per lane
+constexpr int kSelChunk = 4 * 64 * kSelE;       // keys per workgroup
+constexpr int kSelMaxK = 64;
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+  const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+  return ((uint64_t)h2 << 32) | l2;
+}
+
+// Max over the 64 lanes; every lane gets it.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = umax64(v, dpp64<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = umax64(v, dpp64<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = umax64(v, dpp64<0x141>(v));   // row_half_mirror
+  v = umax64(v, dpp64<0x140>(v));   // row_mirror: max of the 16-lane row
+  {
+    // each swap hands a lane its own value and the one of lane l ^ 16 (then l ^ 32)
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    v = umax64(((uint64_t)b[0] << 32) | a[0], ((uint64_t)b[1] << 32) | a[1]);
+  }
+  {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    v = umax64(((uint64_t)b[0] << 32) | a[0], ((uint64_t)b[1] << 32) | a[1]);
+  }
+  return v;
+}
+
+// The k (<= 64) largest of the wave's E x 64 keys, in descending order: lane r
+// returns the r-th (0 for r >= k).  Keys are distinct except the padding key 0.
+template <int E>
+__device__ __forceinline__ uint64_t wave_topk(uint64_t (&x)[E], int k, int lane) {
+  uint64_t m = x[0];
+#pragma unroll
+  for (int e = 1; e < E; ++e) m = umax64(m, x[e]);
+  uint64_t res = 0;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t w = wave_max_u64(m);
+    if (lane == r) res = w;
+    if (m == w) {                        // the owner drops it and finds its next best
+      bool hit = false;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool t = !hit && x[e] == w;
+        x[e] = t ? 0 : x[e];
+        hit = hit || t;
+      }
+      m = x[0];
+#pragma unroll
+      for (int e = 1; e < E; ++e) m = umax64(m, x[e]);
+    }
+  }
+  return res;
+}
+
+template <bool FROM_SCORES, bool FINAL>
+__global__ void __launch_bounds__(kThreads)
+topk_select_kernel(const float* __restrict__ scores, const uint64_t* __restrict__ keys_in, int64_t n_in,
+                   int32_t k, int32_t n_chunks, uint64_t* __restrict__ keys_out, int32_t* __restrict__ ids,
+                   float* __restrict__ out_scores) {
+  __shared__ uint64_t cand[kThreads / 64][64];
+  const int64_t row = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t base = (int64_t)blockIdx.x * kSelChunk + (int64_t)wave * 64 * kSelE + lane;
+  uint64_t x[kSelE];
+#pragma unroll
+  for (int e = 0; e < kSelE; ++e) {
+    const int64_t idx = base + e * 64;
+    uint64_t key = 0;  // below every real key
+    if (idx < n_in) {
+      if (FROM_SCORES) key = make_key(scores[row * n_in + idx], (uint32_t)idx);
+      else key = keys_in[row * n_in + idx];
+    }
+    x[e] = key;
+  }
+  cand[wave][lane] = wave_topk(x, k, lane);
+  __syncthreads();
+  if (wave != 0) return;
+  uint64_t y[kThreads / 64];
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) y[w] = cand[w][lane];
+  const uint64_t key = wave_topk(y, k, lane);
+  if (lane < k) {
+    if (FINAL) {
+      ids[row * k + lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+      if (out_scores) out_scores[row * k + lane] = from_ordered_code((uint32_t)(key >> 32));
+    } else {
+      keys_out[(row * n_chunks + blockIdx.x) * k + lane] = key;
+    }
+  }
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int64_t rows, int32_t n_docs, int32_t k) {
@@ -78,8 +185,45 @@ size_t topk_workspace_bytes(int64_t rows, int32_t n_docs, int32_t k) {
   return (size_t)(2 * ((per + 255) / 256) * 256);
 }
 
+namespace {
+
+hipError_t launch_topk_select(int64_t rows, const float* scores, int32_t n_docs, int32_t k, int32_t* ids,
+                              float* out_scores, void* ws, hipStream_t s) {
+  int64_t n_in = n_docs;
+  int64_t chunks = cdiv(n_in, kSelChunk);
+  if (chunks <= 1) {
+    hipLaunchKernelGGL((topk_select_kernel<true, true>), dim3(1, (unsigned)rows), dim3(kThreads), 0, s, scores,
+                       nullptr, n_in, k, 1, nullptr, ids, out_scores);
+    return hipGetLastError();
+  }
+  // candidates of pass 1 fit in the bitonic path's workspace (its chunks are smaller)
+  const int64_t per = rows * cdiv(n_docs, kChunk) * k * (int64_t)sizeof(uint64_t);
+  uint64_t* buf[2] = {reinterpret_cast<uint64_t*>(ws),
+                      reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + ((per + 255) / 256) * 256)};
+  hipLaunchKernelGGL((topk_select_kernel<true, false>), dim3((unsigned)chunks, (unsigned)rows), dim3(kThreads), 0,
+                     s, scores, nullptr, n_in, k, (int32_t)chunks, buf[0], nullptr, nullptr);
+  int cur = 0;
+  n_in = chunks * k;
+  for (;;) {
+    chunks = cdiv(n_in, kSelChunk);
+    if (chunks <= 1) {
+      hipLaunchKernelGGL((topk_select_kernel<false, true>), dim3(1, (unsigned)rows), dim3(kThreads), 0, s,
+                         nullptr, buf[cur], n_in, k, 1, nullptr, ids, out_scores);
+      break;
+    }
+    hipLaunchKernelGGL((topk_select_kernel<false, false>), dim3((unsigned)chunks, (unsigned)rows), dim3(kThreads),
+                       0, s, nullptr, buf[cur], n_in, k, (int32_t)chunks, buf[cur ^ 1], nullptr, nullptr);
+    cur ^= 1;
+    n_in = chunks * k;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_topk(int64_t rows, const float* scores, int32_t n_docs, int32_t k, int32_t* ids,
                        float* out_scores, void* ws, hipStream_t s) {
+  if (k <= kSelMaxK) return launch_topk_select(rows, scores, n_docs, k, ids, out_scores, ws, s);
   int64_t n_in = n_docs;
   int64_t chunks = cdiv(n_in, kChunk);
   if (chunks <= 1) {

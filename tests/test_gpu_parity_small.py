@@ -154,7 +154,7 @@ def test_topk_multi_pass_and_ties():
     L, B, n_docs = 2, 3, 70001
     sc = np.round(rng.standard_normal((L, B, n_docs)), 2).astype(np.float32)
     sc[0, 0, ::7] = -np.inf
-    for k in (1, 16, 256):
+    for k in (1, 2, 16, 63, 64, 65, 256):
         ws = torch.empty(msa.msa_topk_docs_workspace_size(L, B, n_docs, k), dtype=torch.uint8, device=DEV)
         ids = torch.empty((L, B, k), dtype=torch.int32, device=DEV)
         out = torch.empty((L, B, k), dtype=torch.float32, device=DEV)
@@ -165,6 +165,30 @@ def test_topk_multi_pass_and_ties():
                 ref_ids, ref_sc = O.topk(sc[l, b].astype(np.float64), k)
                 assert ids.cpu().numpy()[l, b].tolist() == ref_ids.tolist()
                 assert np.array_equal(out.cpu().numpy()[l, b], ref_sc.astype(np.float32))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n_docs,k", [(5, 5), (64, 64), (2048, 1), (2048, 64), (2049, 64), (2049, 3),
+                                      (4097, 16), (6144, 64), (131072, 16)])
+def test_topk_chunk_edges(n_docs, k):
+    """Row lengths at and around the selection chunk, k equal to the row length, k at the
+    register path's limit; every score equal in one row (order by id alone)."""
+    print("case: top-k edges n_docs=%d k=%d" % (n_docs, k), flush=True)
+    rng = np.random.default_rng(n_docs * 131 + k)
+    L, B = 2, 2
+    sc = rng.standard_normal((L, B, n_docs)).astype(np.float32)
+    sc[1, 1, :] = 0.25
+    ws = torch.empty(max(1, msa.msa_topk_docs_workspace_size(L, B, n_docs, k)), dtype=torch.uint8, device=DEV)
+    ids = torch.empty((L, B, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((L, B, k), dtype=torch.float32, device=DEV)
+    msa.msa_topk_docs(torch.from_numpy(sc).to(DEV), k, ids, out, ws)
+    torch.cuda.synchronize()
+    ids_h, out_h = ids.cpu().numpy(), out.cpu().numpy()
+    for l in range(L):
+        for b in range(B):
+            ref_ids, ref_sc = O.topk(sc[l, b].astype(np.float64), k)
+            assert ids_h[l, b].tolist() == ref_ids.tolist(), (l, b)
+            assert np.array_equal(out_h[l, b], ref_sc.astype(np.float32))
 
 
 # ----------------------------------------------------------------------- pooling edges
