@@ -9,10 +9,13 @@
 //
 // Layout of the work: one workgroup per (row split, KV head, layer x query) with
 // one wave per query head of the KV head's group.  Each 64-row tile of the KV
-// head's K and V slices is staged in LDS with coalesced 16-byte loads; lane = row
-// for the scores (a wave-wide online-softmax update per tile), lane = 2 output
-// dims for P.V.  Partial (max, sum, acc) per split go to the workspace and a
-// second kernel merges the splits.  All accumulation is fp32.
+// head's K and V slices is staged in LDS with coalesced 16-byte loads, and the
+// next tile's loads are issued before the current tile is used.  Scores: lane =
+// row, a wave-wide online-softmax update per tile (DPP and row-swap reductions).
+// P.V: lane (g, j) sums rows 16 g .. 16 g + 15 into dims 8 j .. 8 j + 7 with
+// 16-byte LDS reads; the four row groups are summed once at the end.  Partial
+// (max, sum, acc) per split go to the workspace and a second kernel merges the
+// splits in one pass.  All accumulation is fp32.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -60,17 +63,23 @@ decode_split_kernel(int32_t Hq, const uint16_t* __restrict__ q, const uint16_t* 
   }
 
   float m_run = -__builtin_huge_valf(), l_run = 0.f;
-  float acc0 = 0.f, acc1 = 0.f;
+  // P.V ownership: lane (g, j) = (lane >> 4, lane & 15) sums rows 16 g .. 16 g + 15 of
+  // each tile into dims 8 j .. 8 j + 7; the four row groups are summed at the end.
+  const int pg = lane >> 4, pj = lane & 15;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const uint16_t* ck = ctx_k + (lb * max_ctx) * (int64_t)kRow + kvh * kDim;
   const uint16_t* cv = ctx_v + (lb * max_ctx) * (int64_t)kRow + kvh * kDim;
   const uint16_t* lk = loc_k + (lb * (int64_t)max_loc) * kRow + kvh * kDim;
   const uint16_t* lv = loc_v + (lb * (int64_t)max_loc) * kRow + kvh * kDim;
 
-  for (int32_t t0 = r_begin; t0 < r_end; t0 += kTileRows) {
+  // Tile loader: 64 rows x 16 chunks of 16 B for K and for V, kPer chunks per thread.
+  constexpr int kPer = kTileRows * 16 / NT;
+  uint4 pk[kPer], pv[kPer];
+  auto load_tile = [&](int32_t t0) {
     const int32_t nr = min(kTileRows, r_end - t0);
-    __syncthreads();
-    // stage K and V: 64 rows x 16 chunks of 16 B each
-    for (int u = tid; u < kTileRows * 16; u += NT) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = tid + i * NT;
       const int rr = u >> 4, c = u & 15;
       uint4 kw = make_uint4(0, 0, 0, 0), vw = kw;
       if (rr < nr) {
@@ -80,10 +89,28 @@ decode_split_kernel(int32_t Hq, const uint16_t* __restrict__ q, const uint16_t* 
         kw = *reinterpret_cast<const uint4*>(ks + c * 8);
         vw = *reinterpret_cast<const uint4*>(vs + c * 8);
       }
-      *reinterpret_cast<uint4*>(k_s + rr * kKStride + c * 8) = kw;
-      *reinterpret_cast<uint4*>(v_s + rr * kDim + c * 8) = vw;
+      pk[i] = kw;
+      pv[i] = vw;
     }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = tid + i * NT;
+      const int rr = u >> 4, c = u & 15;
+      *reinterpret_cast<uint4*>(k_s + rr * kKStride + c * 8) = pk[i];
+      *reinterpret_cast<uint4*>(v_s + rr * kDim + c * 8) = pv[i];
+    }
+  };
+
+  if (r_begin < r_end) load_tile(r_begin);
+  for (int32_t t0 = r_begin; t0 < r_end; t0 += kTileRows) {
+    const int32_t nr = min(kTileRows, r_end - t0);
+    __syncthreads();   // the previous tile's readers are done
+    store_tile();
     __syncthreads();
+    // the next tile's loads stay in flight while this one is scored
+    if (t0 + kTileRows < r_end) load_tile(t0 + kTileRows);
     // scores: lane = row
     float s = -__builtin_huge_valf();
     if (lane < nr) {
@@ -99,32 +126,45 @@ decode_split_kernel(int32_t Hq, const uint16_t* __restrict__ q, const uint16_t* 
       }
       s = d * scale;
     }
-    const float m_tile = wave_max(s);
+    const float m_tile = rows4_max(row16_max(s));
     const float m_new = fmaxf(m_run, m_tile);          // finite: the tile has >= 1 row
     const float alpha = __expf(m_run - m_new);          // 0 when m_run = -inf
-    const float p = lane < nr ? __expf(s - m_new) : 0.f;
-    l_run = l_run * alpha + wave_sum(p);
+    const float p = lane < nr ? __expf(s - m_new) : 0.f;   // rows past the tile's end weigh 0
+    l_run = l_run * alpha + rows4_sum(row16_sum(p));
     m_run = m_new;
     p_s[hh * kTileRows + lane] = p;
     __syncthreads();
-    // P.V: lane owns dims 2*lane, 2*lane+1
-    float a0 = acc0 * alpha, a1 = acc1 * alpha;
-    const float* pp = p_s + hh * kTileRows;
-    for (int rr = 0; rr < nr; ++rr) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(v_s + rr * kDim + 2 * lane);
-      const float pr = pp[rr];
-      a0 += pr * bf16_lo(w);
-      a1 += pr * bf16_hi(w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+    const float4* pp = reinterpret_cast<const float4*>(p_s + hh * kTileRows + 16 * pg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 pr4 = pp[i];
+      const float prs[4] = {pr4.x, pr4.y, pr4.z, pr4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // rows past the tile's end were staged as zeros and carry p = 0
+        const uint4 w = *reinterpret_cast<const uint4*>(v_s + (16 * pg + 4 * i + r) * kDim + 8 * pj);
+        const float pr = prs[r];
+        acc[0] += pr * bf16_lo(w.x); acc[1] += pr * bf16_hi(w.x);
+        acc[2] += pr * bf16_lo(w.y); acc[3] += pr * bf16_hi(w.y);
+        acc[4] += pr * bf16_lo(w.z); acc[5] += pr * bf16_hi(w.z);
+        acc[6] += pr * bf16_lo(w.w); acc[7] += pr * bf16_hi(w.w);
+      }
     }
-    acc0 = a0;
-    acc1 = a1;
   }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = rows4_sum(acc[e]);
   const int64_t part = ((lb * kHeads + kvh) * n_splits + split) * G + hh;
   if (lane == 0) {
     ws_ml[2 * part] = m_run;
     ws_ml[2 * part + 1] = l_run;
   }
-  reinterpret_cast<float2*>(ws_acc + part * kDim)[lane] = make_float2(acc0, acc1);
+  if (pg == 0) {
+    float4* dst = reinterpret_cast<float4*>(ws_acc + part * kDim + 8 * pj);
+    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
 }
 
 __global__ void __launch_bounds__(256)
@@ -135,19 +175,35 @@ decode_merge_kernel(int32_t Hq, int32_t G, int32_t n_splits, const float* __rest
   if (i >= Hq * kDim) return;
   const int hq = i / kDim, d = i % kDim;
   const int kvh = hq / G, hh = hq % G;
-  float M = -__builtin_huge_valf();
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t part = ((lb * kHeads + kvh) * n_splits + s) * G + hh;
-    M = fmaxf(M, ws_ml[2 * part]);
-  }
-  float num = 0.f, den = 0.f;
-  if (M != -__builtin_huge_valf()) {
-    for (int s = 0; s < n_splits; ++s) {
-      const int64_t part = ((lb * kHeads + kvh) * n_splits + s) * G + hh;
-      const float w = __expf(ws_ml[2 * part] - M);
-      num += w * ws_acc[part * kDim + d];
-      den += w * ws_ml[2 * part + 1];
+  // one pass with a running maximum over batches of 8 splits (their loads are
+  // independent); empty splits carry (max = -inf, sum = 0)
+  const float ninf = -__builtin_huge_valf();
+  float M = ninf, num = 0.f, den = 0.f;
+  const int64_t part0 = (lb * kHeads + kvh) * n_splits * G + hh;
+  for (int s0 = 0; s0 < n_splits; s0 += 8) {
+    float m[8], l[8], a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t part = part0 + (int64_t)(s0 + u) * G;
+      const bool ok = s0 + u < n_splits;
+      m[u] = ok ? ws_ml[2 * part] : ninf;
+      l[u] = ok ? ws_ml[2 * part + 1] : 0.f;
+      a[u] = ok ? ws_acc[part * kDim + d] : 0.f;
     }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) Mn = fmaxf(Mn, m[u]);
+    if (Mn == ninf) continue;
+    const float c = __expf(M - Mn);   // 0 while M = -inf
+    num *= c;
+    den *= c;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = __expf(m[u] - Mn);   // 0 for empty splits
+      num += w * a[u];
+      den += w * l[u];
+    }
+    M = Mn;
   }
   out[(lb * Hq + hq) * kDim + d] = den > 0.f ? num / den : 0.f;
 }

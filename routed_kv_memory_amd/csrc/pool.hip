@@ -7,11 +7,14 @@
 // "【MSA】突破100M Token 上下文…", 3.3.2; xiaohongrsx.github.io "MSA paper reading",
 // 方法拆解).
 //
-// One workgroup pools one 16-block tile of one layer.  A block row is 2 KiB =
-// 128 lanes x 16 B, so each half of the workgroup owns one block at a time and
-// every token row is read with one fully coalesced 16-byte load per lane; the
-// three tensors are summed in fp32 in registers (HBM-bound: every input byte is
-// read once).
+// One 512-thread workgroup pools one 16-block tile of one layer; wave w pools
+// blocks w and w + 8.  Lane l owns 16-byte chunks l and 64 + l of each 2 KiB token
+// row, so every row is two contiguous 1 KiB wave loads (nontemporal: each input
+// byte is read once), four tokens in flight per step, summed in fp32 in registers.
+// The tile's outputs (K-bar and V-bar rows, routing keys in the route layout) are
+// staged in LDS and written as three contiguous 32 KiB runs at the end: writes
+// interleaved finely with the read stream, and the route layout's scattered
+// 16-byte pieces, cost far more HBM time than their size.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -26,6 +29,13 @@ __device__ __forceinline__ int32_t find_doc(const int64_t* __restrict__ off, int
     if (off[mid] <= x) lo = mid; else hi = mid;
   }
   return lo;
+}
+
+// Token rows are read exactly once: nontemporal loads keep them from displacing
+// useful lines in the caches.
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 __device__ __forceinline__ void add8(float* acc, uint4 w) {
@@ -51,7 +61,9 @@ __device__ __forceinline__ uint4 mean8(const float* acc, float n, float* ss) {
   return make_uint4(p[0], p[1], p[2], p[3]);
 }
 
-__global__ void __launch_bounds__(256) pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
+constexpr int kU = 4;   // tokens per unrolled step
+
+__global__ void __launch_bounds__(512) pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                    const uint4* __restrict__ kr, int64_t n_tok,
                                                    const int64_t* __restrict__ tok_off,
                                                    const int64_t* __restrict__ blk_off, int32_t n_docs,
@@ -60,6 +72,7 @@ __global__ void __launch_bounds__(256) pool_kernel(const uint4* __restrict__ k, 
                                                    float* __restrict__ krn) {
   __shared__ int64_t s_t0[kTile];
   __shared__ int32_t s_n[kTile];
+  __shared__ uint4 s_out[3][kTileElems / 8];   // the tile's K-bar, V-bar rows and route-layout keys
   const int64_t tile = blockIdx.x;
   const int64_t layer = blockIdx.y;
   const int tid = threadIdx.x;
@@ -82,48 +95,67 @@ __global__ void __launch_bounds__(256) pool_kernel(const uint4* __restrict__ k, 
   }
   __syncthreads();
 
-  const int half = tid >> 7;      // which block of the pair
-  const int c16 = tid & 127;      // 16-byte chunk of the 2 KiB row: head c16/16, dims (c16%16)*8
-  const int h = c16 >> 4, c = c16 & 15;
+  const int wave = tid >> 6, lane = tid & 63;
   const uint4* kl = k + layer * n_tok * (kRow / 8);
   const uint4* vl = v + layer * n_tok * (kRow / 8);
   const uint4* rl = kr + layer * n_tok * (kRow / 8);
-  for (int b = half; b < kTile; b += 2) {
+  for (int b = wave; b < kTile; b += 8) {
     const int64_t blk = tile * kTile + b;
     const int64_t t0 = s_t0[b];
     const int32_t n = s_n[b];
-    float ak[8] = {}, av[8] = {}, ar[8] = {};
+    float ak[2][8] = {}, av[2][8] = {}, ar[2][8] = {};
     int32_t t = 0;
-    for (; t + 4 <= n; t += 4) {
-      uint4 wk[4], wv[4], wr[4];
+    for (; t + kU <= n; t += kU) {
+      uint4 wk[kU][2], wv[kU][2], wr[kU][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t row = (t0 + t + u) * (kRow / 8) + c16;
-        wk[u] = kl[row]; wv[u] = vl[row]; wr[u] = rl[row];
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int64_t row = (t0 + t + u) * (kRow / 8) + hh * 64 + lane;
+          wk[u][hh] = ld_nt(kl + row); wv[u][hh] = ld_nt(vl + row); wr[u][hh] = ld_nt(rl + row);
+        }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) { add8(ak[hh], wk[u][hh]); add8(av[hh], wv[u][hh]); add8(ar[hh], wr[u][hh]); }
+    }
+    for (; t < n; ++t)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int64_t row = (t0 + t) * (kRow / 8) + hh * 64 + lane;
+        add8(ak[hh], ld_nt(kl + row)); add8(av[hh], ld_nt(vl + row)); add8(ar[hh], ld_nt(rl + row));
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) { add8(ak, wk[u]); add8(av, wv[u]); add8(ar, wr[u]); }
+    for (int hh = 0; hh < 2; ++hh) {
+      const int c16 = hh * 64 + lane;   // chunk of the row: head c16 / 16, dims (c16 % 16) * 8
+      const int h = c16 >> 4, c = c16 & 15;
+      float ss = 0.f;
+      uint4 ok = make_uint4(0, 0, 0, 0), ov = ok, orr = ok;
+      if (n > 0) {
+        const float fn = (float)n;
+        ok = mean8(ak[hh], fn, nullptr);
+        ov = mean8(av[hh], fn, nullptr);
+        orr = mean8(ar[hh], fn, &ss);
+      }
+      s_out[0][b * (kRow / 8) + c16] = ok;
+      s_out[1][b * (kRow / 8) + c16] = ov;
+      // route layout: [layer][tile][h][c][b][8]
+      s_out[2][h * (kTile * 16) + c * kTile + b] = orr;
+      ss = row16_sum(ss);   // the 16 lanes of a DPP row hold the 16 chunks of head h
+      if (krn && c == 0) krn[((layer * tiles + tile) * kHeads + h) * kTile + b] = sqrtf(ss);
     }
-    for (; t < n; ++t) {
-      const int64_t row = (t0 + t) * (kRow / 8) + c16;
-      add8(ak, kl[row]); add8(av, vl[row]); add8(ar, rl[row]);
+  }
+  __syncthreads();
+  const int64_t nb = n_blk - tile * kTile < kTile ? n_blk - tile * kTile : kTile;   // real blocks in the tile
+  uint4* dk = kbar + (layer * n_blk + tile * kTile) * (kRow / 8);
+  uint4* dv = vbar + (layer * n_blk + tile * kTile) * (kRow / 8);
+  uint4* dr = krt + (layer * tiles + tile) * (kTileElems / 8);
+  for (int i = tid; i < kTileElems / 8; i += 512) {
+    if (i < nb * (kRow / 8)) {
+      dk[i] = s_out[0][i];
+      dv[i] = s_out[1][i];
     }
-    float ss = 0.f;
-    uint4 ok = make_uint4(0, 0, 0, 0), ov = ok, orr = ok;
-    if (n > 0) {
-      const float fn = (float)n;
-      ok = mean8(ak, fn, nullptr);
-      ov = mean8(av, fn, nullptr);
-      orr = mean8(ar, fn, &ss);
-    }
-    if (blk < n_blk) {
-      kbar[(layer * n_blk + blk) * (kRow / 8) + c16] = ok;
-      vbar[(layer * n_blk + blk) * (kRow / 8) + c16] = ov;
-    }
-    // route layout: [layer][tile][h][c][b][8]
-    krt[((layer * tiles + tile) * kHeads + h) * (kTile * 16) + c * kTile + b] = orr;
-    ss = row16_sum(ss);   // the 16 lanes of a DPP row hold the 16 chunks of head h
-    if (krn && c == 0) krn[((layer * tiles + tile) * kHeads + h) * kTile + b] = sqrtf(ss);
+    dr[i] = s_out[2][i];
   }
 }
 
@@ -157,7 +189,7 @@ hipError_t launch_pool(int32_t L, const uint16_t* k, const uint16_t* v, const ui
                        uint16_t* kbar, uint16_t* vbar, uint16_t* krt, float* krn, hipStream_t s) {
   const int64_t tiles = route_tiles(n_blk);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)tiles, (unsigned)L), dim3(256), 0, s,
+  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)tiles, (unsigned)L), dim3(512), 0, s,
                      reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
                      reinterpret_cast<const uint4*>(kr), n_tok, doc_tok_off, doc_blk_off, n_docs, n_blk, tiles,
                      reinterpret_cast<uint4*>(kbar), reinterpret_cast<uint4*>(vbar), reinterpret_cast<uint4*>(krt),
