@@ -226,6 +226,27 @@ def main():
         result["pooled_tokens_per_s"] = round(L * n_tok / (pool_ms * 1e-3), 1)
         result["pool_GBps"] = round(L * n_tok * POOL_BYTES_PER_TOKEN / (pool_ms * 1e-3) / 1e9, 2)
 
+    # Every step of the path against its own bound (mean over the timed steps).
+    def hbm_row(ms, nbytes, note):
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 4), "algorithmic_GB": round(nbytes / 1e9, 4), "GBps": round(gbps, 1),
+                "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes": note}
+    rows = {}
+    if cfg.per_token:
+        rows["A1_pool"] = hbm_row(float(seg_mean[0]), L * n_tok * POOL_BYTES_PER_TOKEN + 3 * L * n_blk * 2048,
+                                  "K, V, Kr token rows read + K-bar, V-bar, Kr-bar rows written")
+    rows["A2_route_scan"] = dict(roofline, ms=round(scan_ms, 4))
+    rows["A3_topk"] = dict(hbm_row(float(seg_mean[2]), L * B * n_docs * 4 + L * B * k * 8, "scores read + ids/scores written"),
+                           bound="latency (%d rows of %d scores)" % (L * B, n_docs))
+    rows["A4_gather"] = dict(hbm_row(float(seg_mean[3]), ctx_rows * 4 * 2048, "K-bar and V-bar rows read + written"),
+                             bound="latency (dependent id -> offset -> row loads)")
+    rows["A5_decode"] = dict(hbm_row(float(seg_mean[4]), dec_rows * DECODE_BYTES_PER_ROW, "K and V rows of 8 heads read"),
+                             bound="hbm")
+    result["rows"] = rows
+    if not args.no_cpu_baseline:
+        result["cpu_rows"] = cpu_rows(cfg, L, B, k, n_docs, blk.numpy(), dsc, ids, kbar, vbar, q, ck, cv, cl, lk,
+                                      lv, ll, scale, pool_args)
+
     if args.calibrate_copy:
         del ck, cv
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -238,6 +259,62 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, n_blk, blk.numpy(), args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def cpu_rows(cfg, L, B, k, n_docs, blk_off, dsc, ids, kbar, vbar, q, ck, cv, cl, lk, lv, ll, scale, pool_args):
+    """The fp64 oracle's top-k, gather, decode (and pooling) on one (layer, query) of the same
+    step's GPU data, single thread, with the whole-step equivalent (x layers x queries)."""
+    import numpy as np
+
+    import oracle as O
+
+    import torch
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    def u16(t):   # bf16 tensor -> its uint16 bit patterns on the host
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    out = {}
+    S = dsc[0, 0].double().cpu().numpy()
+    dt = timed(lambda: O.topk(S, k))
+    out["A3_topk"] = {"sample": "one (layer, query): top-%d of %d scores" % (k, n_docs), "s": round(dt, 6),
+                      "step_equivalent_ms": round(dt * L * B * 1e3, 3)}
+    sel = ids[0, 0].cpu().numpy()
+    kb_parts, vb_parts, off = [], [], [0]
+    for d in sel:
+        b0, b1 = int(blk_off[d]), int(blk_off[d + 1])
+        kb_parts.append(u16(kbar[0, b0:b1]))
+        vb_parts.append(u16(vbar[0, b0:b1]))
+        off.append(off[-1] + b1 - b0)
+    kb_c, vb_c = np.concatenate(kb_parts), np.concatenate(vb_parts)
+    off = np.array(off, np.int64)
+    dt = timed(lambda: O.gather(np.arange(len(sel), dtype=np.int32), off, kb_c, vb_c))
+    out["A4_gather"] = {"sample": "one (layer, query): %d selected documents, %d blocks" % (len(sel), int(off[-1])),
+                        "s": round(dt, 6), "step_equivalent_ms": round(dt * L * B * 1e3, 3)}
+    n_ctx, n_loc = int(cl[0, 0]), int(ll[0, 0])
+    args = (u16(q[0, 0]), u16(ck[0, 0, :n_ctx]), u16(cv[0, 0, :n_ctx]), u16(lk[0, 0, :n_loc]), u16(lv[0, 0, :n_loc]))
+    dt = timed(lambda: O.decode(*args, scale))
+    out["A5_decode"] = {"sample": "one (layer, query): %d query heads over %d + %d rows" % (q.shape[2], n_ctx, n_loc),
+                        "s": round(dt, 6), "step_equivalent_ms": round(dt * L * B * 1e3, 3)}
+    if pool_args is not None:
+        kt, vt, krt_, tok_d = pool_args[0], pool_args[1], pool_args[2], pool_args[3]
+        tok = tok_d.cpu().numpy()
+        nd = min(len(tok) - 1, 40)
+        t_end = int(tok[nd])
+        sub_tok = tok[: nd + 1]
+        sub_blk, _, _ = O.block_offsets(sub_tok)
+        xs = [u16(a[0:1, :t_end]) for a in (kt, vt, krt_)]
+        dt = timed(lambda: [O.pool(x, sub_tok, sub_blk) for x in xs])
+        n_tok = int(tok[-1])
+        out["A1_pool"] = {"sample": "layer 0, documents 0..%d (%d tokens), K, V and Kr" % (nd - 1, t_end),
+                          "s": round(dt, 6), "step_equivalent_ms": round(dt * L * n_tok / t_end * 1e3, 1)}
+    out["cores"] = 1
+    out["kind"] = "oracle"
+    return out
 
 
 def cpu_baseline(cfg, n_blk, blk_off, seconds):
