@@ -241,3 +241,20 @@ void orc_decode(int32_t Hq, const uint16_t* q,
     }
     free(s);
 }
+
+/* ---------------------------------------------------------------- prefill */
+
+void orc_prefill(int32_t T, int32_t Hq, const uint16_t* q,
+                 const uint16_t* ctx_k, const uint16_t* ctx_v, int64_t n_ctx,
+                 const uint16_t* loc_k, const uint16_t* loc_v, int64_t n_loc,
+                 double scale, double* out)
+{
+    for (int32_t t = 0; t < T; ++t) {
+        /* local rows visible to token t: 0 .. n_loc - T + t */
+        int64_t vis = n_loc - T + t + 1;
+        if (vis < 0) vis = 0;
+        if (vis > n_loc) vis = n_loc;
+        orc_decode(Hq, q + (size_t)t * Hq * ORC_D, ctx_k, ctx_v, n_ctx, loc_k, loc_v, vis, scale,
+                   out + (size_t)t * Hq * ORC_D);
+    }
+}

@@ -33,6 +33,8 @@
  *   orc_topk                                    pinned (brute-force sort, ties, permutation)
  *   orc_gather                                  pinned (library concatenation)
  *   orc_decode                                  pinned (single key, equal keys, q=0, library softmax, permutation)
+ *   orc_prefill                                 pinned (library masked attention, T = 1 is decode, causality,
+ *                                               single visible row)
  */
 #ifndef MSA_ORACLE_H
 #define MSA_ORACLE_H
@@ -113,6 +115,20 @@ void orc_decode(int32_t Hq, const uint16_t* q,
                 const uint16_t* ctx_k, const uint16_t* ctx_v, int64_t n_ctx,
                 const uint16_t* loc_k, const uint16_t* loc_v, int64_t n_loc,
                 double scale, double* out);
+
+/* [P2 5.2 (the layer's attention runs varlen flash attention over the query states
+ * and the concatenation of local and selected K/V); P1 推理流水线 (Stage 2 prefills
+ * the assembled sparse context)] Multi-token sparse prefill: T query tokens, the
+ * last T of the n_loc local rows, each attend to every memory-context row and,
+ * causally, to local rows 0 .. n_loc - T + t (the pages name no mask; this is the
+ * causal reading aligned to the end of the local part, so T = 1 is orc_decode).
+ * Token t is computed exactly as orc_decode over [ctx ; local rows visible to t].
+ * q: [T][Hq][128]; ctx_*: [n_ctx][8][128]; loc_*: [n_loc][8][128], n_loc >= T;
+ * out: [T][Hq][128]. */
+void orc_prefill(int32_t T, int32_t Hq, const uint16_t* q,
+                 const uint16_t* ctx_k, const uint16_t* ctx_v, int64_t n_ctx,
+                 const uint16_t* loc_k, const uint16_t* loc_v, int64_t n_loc,
+                 double scale, double* out);
 
 #ifdef __cplusplus
 }

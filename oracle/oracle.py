@@ -60,6 +60,7 @@ def lib():
         L.orc_gather.argtypes = [P, i32, P, P, P, P, P]
         L.orc_gather.restype = i64
         L.orc_decode.argtypes = [i32, P, P, P, i64, P, P, i64, f64, P]
+        L.orc_prefill.argtypes = [i32, i32, P, P, P, i64, P, P, i64, f64, P]
         _lib = L
     return _lib
 
@@ -217,6 +218,21 @@ def decode(q, ctx_k, ctx_v, loc_k, loc_v, scale: float) -> np.ndarray:
     return out
 
 
+def prefill(q, ctx_k, ctx_v, loc_k, loc_v, scale: float) -> np.ndarray:
+    """One (layer, query): q [T][Hq][128]; ctx rows [n_ctx][8][128]; local rows [n_loc][8][128]
+    (the query tokens are the last T of them) -> out [T][Hq][128] float64."""
+    q = _u16(q)
+    T, Hq = q.shape[0], q.shape[1]
+    ck, cv, lk, lv = _u16(ctx_k), _u16(ctx_v), _u16(loc_k), _u16(loc_v)
+    n_ctx, n_loc = ck.shape[0], lk.shape[0]
+    assert n_loc >= T
+    one = np.zeros((1, H, D), np.uint16)
+    ck_, cv_ = (ck, cv) if n_ctx else (one, one)
+    out = np.empty((T, Hq, D), np.float64)
+    lib().orc_prefill(T, Hq, _p(q), _p(ck_), _p(cv_), n_ctx, _p(lk), _p(lv), n_loc, float(scale), _p(out))
+    return out
+
+
 __all__ = ["build", "lib", "bf16_to_f64", "bf16_from_f64", "bf16_from_f64_scalar", "group_ids",
            "doc_tok_offsets", "block_offsets", "pool", "head_norms", "block_score", "doc_scores",
-           "doc_scores_all", "topk", "gather", "decode", "H", "D", "BLOCK", "ROW"]
+           "doc_scores_all", "topk", "gather", "decode", "prefill", "H", "D", "BLOCK", "ROW"]

@@ -394,3 +394,69 @@ def test_decode_no_rows_is_zero(orc):
     e = np.zeros((0, H, D), np.uint16)
     out = orc.decode(np.ones((32, D), np.uint16), e, e, e, e, 0.1)
     assert np.all(out == 0.0)
+
+
+# ------------------------------------------------------------------- prefill
+
+def _prefill_inputs(rng, T, n_ctx, n_loc, Hq=32):
+    q = rand_bf16(rng, (T, Hq, D))
+    ck, cv = rand_bf16(rng, (n_ctx, H, D)), rand_bf16(rng, (n_ctx, H, D))
+    lk, lv = rand_bf16(rng, (n_loc, H, D)), rand_bf16(rng, (n_loc, H, D))
+    return q, ck, cv, lk, lv
+
+
+def test_prefill_matches_library_masked_attention(orc):
+    """torch's scaled_dot_product_attention in float64 with an explicit boolean mask: memory rows
+    always visible, local row j visible to token t iff j <= n_loc - T + t; GQA by repeating KV heads."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(40)
+    T, n_ctx, n_loc, Hq = 6, 7, 9, 16
+    q, ck, cv, lk, lv = _prefill_inputs(rng, T, n_ctx, n_loc, Hq)
+    scale = 1 / math.sqrt(128)
+    out = orc.prefill(q, ck, cv, lk, lv, scale)
+    K = torch.from_numpy(np.concatenate([val(ck), val(lk)]))          # [n, 8, 128]
+    V = torch.from_numpy(np.concatenate([val(cv), val(lv)]))
+    G = Hq // H
+    Kq = K.permute(1, 0, 2).repeat_interleave(G, dim=0)                # [Hq, n, 128]
+    Vq = V.permute(1, 0, 2).repeat_interleave(G, dim=0)
+    Q = torch.from_numpy(val(q)).permute(1, 0, 2)                      # [Hq, T, 128]
+    j = torch.arange(n_ctx + n_loc)
+    t = torch.arange(T)[:, None]
+    mask = (j[None, :] < n_ctx) | (j[None, :] - n_ctx <= n_loc - T + t)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, Kq, Vq, attn_mask=mask, scale=scale)
+    assert np.allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_with_one_token_is_decode_and_last_token_sees_everything(orc):
+    rng = np.random.default_rng(41)
+    q, ck, cv, lk, lv = _prefill_inputs(rng, 5, 4, 8)
+    scale = 0.09
+    out = orc.prefill(q, ck, cv, lk, lv, scale)
+    assert np.array_equal(out[4], orc.decode(q[4], ck, cv, lk, lv, scale))
+    assert np.array_equal(orc.prefill(q[:1], ck, cv, lk, lv, scale)[0], orc.decode(q[0], ck, cv, lk, lv, scale))
+
+
+def test_prefill_is_causal_in_the_local_rows(orc):
+    """Changing local row r changes exactly the tokens that may see it."""
+    rng = np.random.default_rng(42)
+    T, n_ctx, n_loc = 6, 3, 10
+    q, ck, cv, lk, lv = _prefill_inputs(rng, T, n_ctx, n_loc)
+    base = orc.prefill(q, ck, cv, lk, lv, 0.1)
+    for r in (0, 4, 5, 9):
+        lk2, lv2 = lk.copy(), lv.copy()
+        lk2[r] = rand_bf16(rng, (H, D))
+        lv2[r] = rand_bf16(rng, (H, D))
+        out = orc.prefill(q, ck, cv, lk2, lv2, 0.1)
+        for t in range(T):
+            sees = r <= n_loc - T + t
+            assert np.array_equal(out[t], base[t]) != sees, (r, t)
+
+
+def test_prefill_first_token_of_a_bare_query_sees_one_row(orc):
+    """No memory rows and local = the query itself: token 0 attends to local row 0 alone."""
+    rng = np.random.default_rng(43)
+    T = 4
+    q, ck, cv, lk, lv = _prefill_inputs(rng, T, 0, T)
+    out = orc.prefill(q, ck, cv, lk, lv, 0.1)
+    for hq in range(32):
+        assert np.array_equal(out[0, hq], val(lv[0, hq // 4]))
