@@ -235,6 +235,31 @@ int msa_sparse_decode(int32_t n_layers, int32_t B, int32_t Hq, const uint16_t* q
                       int32_t max_loc, float scale, float* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ multi-token prefill
+ *
+ * [P2 5.2 (varlen attention over the query states and the concatenation of local and
+ * selected K/V); P1 推理流水线 (Stage 2 prefills the assembled sparse context)]  T query
+ * tokens of grouped-query attention per (layer, query).  The query tokens are the last
+ * T of the local rows: token t sees every memory-context row and the local rows
+ * 0 .. loc_len - T + t (causal, aligned to the end of the local part; with T = 1 this is
+ * msa_sparse_decode).  Query head hq reads KV head hq / (Hq / 8); softmax scale as
+ * given; online softmax in fp32; the probabilities enter the P.V product as a bf16
+ * high part plus a bf16 residual (~16 significant bits).
+ *
+ *   q            [n_layers][B][T][Hq][128] bf16, Hq in {8, 16, 32, 64}
+ *   ctx_k, ctx_v [n_layers][B][max_ctx][8][128] bf16;  ctx_len [n_layers][B] int32
+ *   loc_k, loc_v [n_layers][B][max_loc][8][128] bf16;  loc_len [n_layers][B] int32
+ *   out          [n_layers][B][T][Hq][128] fp32 (zero for a token that sees no row)
+ *
+ * Lengths are clamped to [0, max_ctx] / [0, max_loc].  No workspace.  Errors: NULL
+ * pointers, sizes < 1, max_loc < T, Hq % 8 != 0 (SHAPE), Hq > 64 or n_layers * B >
+ * 65535 (UNSUPPORTED). */
+int msa_sparse_prefill(int32_t n_layers, int32_t B, int32_t T, int32_t Hq, const uint16_t* q,
+                       const uint16_t* ctx_k, const uint16_t* ctx_v, const int32_t* ctx_len,
+                       int32_t max_ctx,
+                       const uint16_t* loc_k, const uint16_t* loc_v, const int32_t* loc_len,
+                       int32_t max_loc, float scale, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

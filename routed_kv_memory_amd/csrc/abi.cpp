@@ -282,3 +282,21 @@ MSA_API int msa_sparse_decode(int32_t n_layers, int32_t B, int32_t Hq, const uin
                                        max_loc, scale, out, workspace, as_stream(stream)),
                     "msa_sparse_decode");
 }
+
+MSA_API int msa_sparse_prefill(int32_t n_layers, int32_t B, int32_t T, int32_t Hq, const uint16_t* q,
+                               const uint16_t* ctx_k, const uint16_t* ctx_v, const int32_t* ctx_len, int32_t max_ctx,
+                               const uint16_t* loc_k, const uint16_t* loc_v, const int32_t* loc_len, int32_t max_loc,
+                               float scale, float* out, void* stream) {
+  if (!q || !ctx_k || !ctx_v || !ctx_len || !loc_k || !loc_v || !loc_len || !out)
+    return fail(MSA_ERR_NULL, "msa_sparse_prefill: null pointer");
+  if (n_layers < 1 || B < 1 || T < 1 || Hq < 1 || max_ctx < 1 || max_loc < T || Hq % MSA_HEADS != 0)
+    return fail(MSA_ERR_SHAPE, "msa_sparse_prefill: n_layers=%d B=%d T=%d Hq=%d max_ctx=%d max_loc=%d", n_layers,
+                B, T, Hq, max_ctx, max_loc);
+  const int G = Hq / MSA_HEADS;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8))
+    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_prefill: Hq=%d (supported: 8, 16, 32, 64)", Hq);
+  if ((int64_t)n_layers * B > 65535) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_prefill: n_layers*B > 65535");
+  return hip_status(msa::launch_prefill(n_layers, B, T, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx, loc_k, loc_v, loc_len,
+                                        max_loc, scale, out, as_stream(stream)),
+                    "msa_sparse_prefill");
+}

@@ -43,5 +43,9 @@ hipError_t launch_decode(int32_t L, int32_t B, int32_t Hq, const uint16_t* q, co
                          const uint16_t* ctx_v, const int32_t* ctx_len, int32_t max_ctx, const uint16_t* loc_k,
                          const uint16_t* loc_v, const int32_t* loc_len, int32_t max_loc, float scale, float* out,
                          void* ws, hipStream_t s);
+hipError_t launch_prefill(int32_t L, int32_t B, int32_t T, int32_t Hq, const uint16_t* q, const uint16_t* ctx_k,
+                          const uint16_t* ctx_v, const int32_t* ctx_len, int32_t max_ctx, const uint16_t* loc_k,
+                          const uint16_t* loc_v, const int32_t* loc_len, int32_t max_loc, float scale, float* out,
+                          hipStream_t s);
 
 }  // namespace msa

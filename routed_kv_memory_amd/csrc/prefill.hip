@@ -1,0 +1,245 @@
+// prefill.hip -- multi-token sparse prefill: T query tokens of grouped-query
+// attention over [memory context ; local KV], causal in the local part.
+//
+// Method: after routing, the layer's attention runs over the query states and the
+// concatenation of the selected documents' compressed K/V with the local K/V
+// (xuqi2024.github.io "【MSA】突破100M Token 上下文…", 5.2; yunpan.plus
+// "MSA端到端可训练记忆模型完整开源…", 推理流水线, Stage 2).  Query token t is the
+// (n_loc - T + t)-th local row: it sees every memory-context row and local rows
+// 0 .. n_loc - T + t.
+//
+// Layout of the work: one workgroup per (16-token query block, KV head, layer x
+// query), one wave per query head of the KV head's group, so the waves share the
+// K/V tiles and the causal mask.  Per 32-key tile (K and V row-major, staged in
+// LDS; the next tile's loads are issued before the current tile is
+// used) a wave computes S^T = K . Q^T with v_mfma_f32_16x16x32_bf16 (keys as the A
+// operand, the query block as the B operand held in registers): lane l owns query
+// token l & 15 and keys 4 (l >> 4) + r of each 16-key half.  The online softmax
+// runs on those fp32 scores (cross-lane max over the four lane groups, per-lane
+// partial sums).  For O^T += V^T . P^T the MFMA's 32-long k axis is taken in the
+// order (first half: keys 4g..4g+3, second half: keys 16+4g..16+4g+3) for lane
+// group g, which is exactly how the score accumulators already sit in the lanes,
+// so P enters as the B operand without any shuffle; V^T comes from the row-major
+// V tile in the same key order through LDS transposed reads (ds_read_b64_tr_b16).  P goes in as a bf16 high part plus a bf16
+// residual (two products), so the probabilities keep ~16 significant bits.
+// Accumulation is fp32 throughout.
+#include "msa_device.hpp"
+#include "msa_kernels.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int kQBlock = 16;            // query tokens per workgroup
+constexpr int kKeyTile = 32;           // keys per step
+constexpr int kKStride = kDim + 8;     // bf16 per staged K row
+constexpr int kVStride = kDim + 8;     // bf16 per staged V row
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the
+// 8-byte chunks addressed by lanes 4 e + i / 4 (e = 0..3) -- a 16 x 4 transpose of
+// 16-bit elements.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+template <int G>
+__global__ void __launch_bounds__(64 * G)
+prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint16_t* __restrict__ ctx_k,
+               const uint16_t* __restrict__ ctx_v, const int32_t* __restrict__ ctx_len, int32_t max_ctx,
+               const uint16_t* __restrict__ loc_k, const uint16_t* __restrict__ loc_v,
+               const int32_t* __restrict__ loc_len, int32_t max_loc, float scale, float* __restrict__ out) {
+  __shared__ uint16_t k_s[kKeyTile * kKStride];
+  __shared__ uint16_t v_s[kKeyTile * kVStride];
+
+  constexpr int NT = 64 * G;
+  const int t0 = blockIdx.x * kQBlock;
+  const int kvh = blockIdx.y;
+  const int64_t lb = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int hh = tid >> 6;                 // query head within the group (= wave)
+  const int lane = tid & 63;
+  const int g = lane >> 4, j = lane & 15;  // lane group, query token t0 + j
+  const float ninf = -__builtin_huge_valf();
+
+  int32_t clen = ctx_len[lb];
+  clen = clen < 0 ? 0 : (clen > max_ctx ? max_ctx : clen);
+  int32_t llen = loc_len[lb];
+  llen = llen < 0 ? 0 : (llen > max_loc ? max_loc : llen);
+  // local rows visible to token t: 0 .. llen - T + t (clamped to [0, llen])
+  auto visible = [&](int t) {
+    int v = llen - T + t + 1;
+    return v < 0 ? 0 : (v > llen ? llen : v);
+  };
+  const int t_last = t0 + kQBlock - 1 < T - 1 ? t0 + kQBlock - 1 : T - 1;
+  const int32_t n_keys = clen + visible(t_last);
+  const int tok = t0 + j;
+  const int vis_tok = tok < T ? visible(tok) : 0;
+
+  // query block as B fragments: token t0 + j, dims 32 s + 8 g .. +7
+  const int hq = kvh * G + hh;
+  bf16x8 qf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (tok < T) v = *reinterpret_cast<const u32x4*>(q + (((lb * T + tok) * Hq + hq) * kDim) + 32 * s + 8 * g);
+    qf[s] = __builtin_bit_cast(bf16x8, v);
+  }
+
+  const uint16_t* ck = ctx_k + (lb * max_ctx) * (int64_t)kRow + kvh * kDim;
+  const uint16_t* cv = ctx_v + (lb * max_ctx) * (int64_t)kRow + kvh * kDim;
+  const uint16_t* lk = loc_k + (lb * (int64_t)max_loc) * kRow + kvh * kDim;
+  const uint16_t* lv = loc_v + (lb * (int64_t)max_loc) * kRow + kvh * kDim;
+
+  // tile loader: 32 keys x 16 chunks of 16 B for K and for V
+  constexpr int kPer = (kKeyTile * 16 + NT - 1) / NT;
+  uint4 pk[kPer], pv[kPer];
+  auto load_tile = [&](int32_t k0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = tid + i * NT;
+      const int kk = u >> 4, c = u & 15;
+      uint4 kw = make_uint4(0, 0, 0, 0), vw = kw;
+      const int32_t row = k0 + kk;
+      if (u < kKeyTile * 16 && row < n_keys) {
+        const uint16_t* ks = row < clen ? ck + (int64_t)row * kRow : lk + (int64_t)(row - clen) * kRow;
+        const uint16_t* vs = row < clen ? cv + (int64_t)row * kRow : lv + (int64_t)(row - clen) * kRow;
+        kw = *reinterpret_cast<const uint4*>(ks + c * 8);
+        vw = *reinterpret_cast<const uint4*>(vs + c * 8);
+      }
+      pk[i] = kw;
+      pv[i] = vw;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = tid + i * NT;
+      if (u >= kKeyTile * 16) break;
+      const int kk = u >> 4, c = u & 15;
+      *reinterpret_cast<uint4*>(k_s + kk * kKStride + c * 8) = pk[i];
+      *reinterpret_cast<uint4*>(v_s + kk * kVStride + c * 8) = pv[i];
+    }
+  };
+
+  float m_run = ninf, l_lane = 0.f;
+  f32x4 o[8];   // O^T: dims 16 dt + 4 g + r, token t0 + j
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (n_keys > 0) load_tile(0);
+  for (int32_t k0 = 0; k0 < n_keys; k0 += kKeyTile) {
+    __syncthreads();   // the previous tile's readers are done
+    store_tile();
+    __syncthreads();
+    if (k0 + kKeyTile < n_keys) load_tile(k0 + kKeyTile);
+
+    // S^T for keys k0 + 16 h2 + 4 g + r (h2 = 0, 1), token t0 + j
+    f32x4 sc[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(k_s + (16 * h2 + j) * kKStride + 32 * s + 8 * g);
+        sc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[s], sc[h2], 0, 0, 0);
+      }
+    }
+    // scale and mask
+    float mt = ninf;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int32_t key = k0 + 16 * h2 + 4 * g + r;
+        const bool ok = key < n_keys && (key < clen || key - clen < vis_tok);
+        const float v = ok ? sc[h2][r] * scale : ninf;
+        sc[h2][r] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = rows4_max(mt);                      // over the tile's 32 keys of token t0 + j
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == ninf ? 0.f : m_new;   // a token with no visible key yet
+    const float alpha = __expf(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __expf(sc[h2][r] - m_use);
+        sc[h2][r] = p;
+        psum += p;
+      }
+    l_lane = l_lane * alpha + psum;
+    m_run = m_new;
+    // P^T as the B operand: k slot 8 g + e holds key 4 g + e (e < 4) or 16 + 4 g + e - 4.
+    // P = P_hi + P_lo with both parts in bf16 (two products), so the probabilities
+    // enter the matrix cores with ~16 significant bits rather than 8.
+    u32x4 pwh, pwl;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float p0 = sc[e2 >> 1][2 * (e2 & 1)], p1 = sc[e2 >> 1][2 * (e2 & 1) + 1];
+      const uint32_t hw = pack2_bf16(p0, p1);
+      pwh[e2] = hw;
+      pwl[e2] = pack2_bf16(p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u));
+    }
+    const bf16x8 pfh = __builtin_bit_cast(bf16x8, pwh), pfl = __builtin_bit_cast(bf16x8, pwl);
+    // V^T fragments by transposed reads of the row-major V tile: lane (g, j) of the
+    // A operand needs dim 16 dt + j of keys 4 g + e and 16 + 4 g + e (e = 0..3), so
+    // source lane j points at dims 16 dt + 4 (j & 3) .. +3 of key 4 g + (j >> 2).
+    const uint16_t* vsrc = v_s + (4 * g + (j >> 2)) * kVStride + 4 * (j & 3);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint2 a0 = lds_read_tr16(vsrc + 16 * dt);
+      const uint2 a1 = lds_read_tr16(vsrc + 16 * kVStride + 16 * dt);
+      const u32x4 vw = {a0.x, a0.y, a1.x, a1.y};
+      o[dt] *= alpha;
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vw), pfh, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vw), pfl, o[dt], 0, 0, 0);
+    }
+  }
+
+  const float l_tok = rows4_sum(l_lane);
+  if (tok < T) {
+    const float inv = l_tok > 0.f ? 1.0f / l_tok : 0.f;
+    float* dst = out + ((lb * T + tok) * Hq + hq) * kDim + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(dst + 16 * dt) =
+          make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(int32_t L, int32_t B, int32_t T, int32_t Hq, const uint16_t* q, const uint16_t* ctx_k,
+                          const uint16_t* ctx_v, const int32_t* ctx_len, int32_t max_ctx, const uint16_t* loc_k,
+                          const uint16_t* loc_v, const int32_t* loc_len, int32_t max_loc, float scale, float* out,
+                          hipStream_t s) {
+  const int G = Hq / kHeads;
+  const dim3 grid((unsigned)((T + kQBlock - 1) / kQBlock), kHeads, (unsigned)(L * B));
+  switch (G) {
+    case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(64), 0, s, T, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
+                               loc_k, loc_v, loc_len, max_loc, scale, out); break;
+    case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(128), 0, s, T, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
+                               loc_k, loc_v, loc_len, max_loc, scale, out); break;
+    case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(256), 0, s, T, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
+                               loc_k, loc_v, loc_len, max_loc, scale, out); break;
+    case 8: hipLaunchKernelGGL(prefill_kernel<8>, grid, dim3(512), 0, s, T, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
+                               loc_k, loc_v, loc_len, max_loc, scale, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

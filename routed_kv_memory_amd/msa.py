@@ -46,6 +46,8 @@ _SIGS = {
     "msa_sparse_decode_workspace_size": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_decode": ([_I32, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _F32, _P, _P, _SZ, _P],
                           ctypes.c_int),
+    "msa_sparse_prefill": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _F32, _P, _P],
+                           ctypes.c_int),
 }
 
 _lib = None
@@ -227,3 +229,13 @@ def msa_sparse_decode(q, ctx_k, ctx_v, ctx_len, loc_k, loc_v, loc_len, scale, ou
         _ptr(loc_len, _I32T, "loc_len", allow_none=True), max_loc, float(scale),
         _ptr(out, _F32T, "out"), _ptr(workspace, _ANY, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def msa_sparse_prefill(q, ctx_k, ctx_v, ctx_len, loc_k, loc_v, loc_len, scale, out, stream=None):
+    """q [L][B][T][Hq][128] bf16; contexts as for msa_sparse_decode; out [L][B][T][Hq][128] fp32."""
+    L, B, T, Hq = q.shape[0], q.shape[1], q.shape[2], q.shape[3]
+    _check("msa_sparse_prefill", lib().msa_sparse_prefill(
+        L, B, T, Hq, _ptr(q, _BF16, "q"), _ptr(ctx_k, _BF16, "ctx_k"), _ptr(ctx_v, _BF16, "ctx_v"),
+        _ptr(ctx_len, _I32T, "ctx_len"), ctx_k.shape[2], _ptr(loc_k, _BF16, "loc_k"), _ptr(loc_v, _BF16, "loc_v"),
+        _ptr(loc_len, _I32T, "loc_len"), loc_k.shape[2], float(scale), _ptr(out, _F32T, "out"), _stream(stream)))
+

@@ -91,6 +91,13 @@ def test_invalid_arguments_are_rejected_on_the_host(msa):
                                  fake, fake, 1 << 20, None) == 3                              # group of 3
     assert lib.msa_sparse_decode(1, 1, 32, fake, fake, fake, fake, 16, None, None, None, 4, ctypes.c_float(0.1),
                                  fake, fake, 1 << 20, None) == 1                              # local KV missing
+    # prefill: null, fewer local rows than tokens, unsupported head group
+    assert lib.msa_sparse_prefill(1, 1, 4, 32, None, fake, fake, fake, 8, fake, fake, fake, 4, ctypes.c_float(0.1),
+                                  fake, None) == 1
+    assert lib.msa_sparse_prefill(1, 1, 4, 32, fake, fake, fake, fake, 8, fake, fake, fake, 3, ctypes.c_float(0.1),
+                                  fake, None) == 2
+    assert lib.msa_sparse_prefill(1, 1, 4, 24, fake, fake, fake, fake, 8, fake, fake, fake, 4, ctypes.c_float(0.1),
+                                  fake, None) == 3
     # workspace too small
     need = lib.msa_route_topk_workspace_size(2, 1, 100000, 16)
     assert lib.msa_route_topk(2, fake, 1, 8, fake, 1000, fake, 100000, 16, fake, None, None, fake, need - 1,
