@@ -103,3 +103,33 @@ class DeviceInputs:
         self.gen.fill(lv, cfg.seed, S.S_LOC_V)
         ll = torch.full((cfg.n_layers, cfg.B), cfg.L_loc, dtype=torch.int32, device=self.device)
         return q, lk, lv, ll
+
+    def prefill_inputs(self, max_doc_blocks: int = None):
+        """Inputs of one multi-token prefill at the longest round: q [L][B][T][Hq][128];
+        a memory context [L][B][k * max_doc_blocks][8][128] whose length is the block count of
+        k documents drawn (seeded) from the memory's length mix; local rows = the query
+        itself [L][B][T][8][128], loc_len = T."""
+        cfg, mem = self.cfg, self.mem
+        T = max(cfg.T_rounds) if cfg.T_rounds else cfg.T
+        L, B = cfg.n_layers, cfg.B
+        counts = np.diff(S.prepooled_doc_blk_offsets(mem)) if not mem.per_token else None
+        if counts is None:
+            raise ValueError("prefill inputs need a pre-pooled memory")
+        mdb = int(counts.max()) if max_doc_blocks is None else max_doc_blocks
+        rng = np.random.default_rng(cfg.seed + S.S_PF_DOCS)
+        docs = rng.choice(counts.size, size=(L, B, cfg.k), replace=True)
+        ctx_len = torch.as_tensor(counts[docs].sum(axis=-1).astype(np.int32)).to(self.device)
+        max_ctx = cfg.k * mdb
+        q = torch.empty((L, B, T, cfg.Hq, S.D), dtype=torch.bfloat16, device=self.device)
+        self.gen.fill(q, cfg.seed, S.S_PF_Q)
+        ck = torch.empty((L, B, max_ctx, S.H, S.D), dtype=torch.bfloat16, device=self.device)
+        cv = torch.empty_like(ck)
+        self.gen.fill(ck, cfg.seed, S.S_PF_CTX_K)
+        self.gen.fill(cv, cfg.seed, S.S_PF_CTX_V)
+        lk = torch.empty((L, B, T, S.H, S.D), dtype=torch.bfloat16, device=self.device)
+        lv = torch.empty_like(lk)
+        self.gen.fill(lk, cfg.seed, S.S_LOC_K)
+        self.gen.fill(lv, cfg.seed, S.S_LOC_V)
+        ll = torch.full((L, B), T, dtype=torch.int32, device=self.device)
+        return q, ck, cv, ctx_len, lk, lv, ll
+

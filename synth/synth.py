@@ -47,6 +47,7 @@ S_KBAR, S_VBAR, S_KRBAR = 4, 5, 6   # pre-pooled K-bar, V-bar, routing keys
 S_QR, S_NEEDLE = 7, 8
 S_DEC_Q, S_LOC_K, S_LOC_V = 9, 10, 11
 S_TABLES = 12
+S_PF_Q, S_PF_CTX_K, S_PF_CTX_V, S_PF_DOCS = 13, 14, 15, 16   # multi-token prefill inputs
 
 SEED0 = 0x4D534100
 
