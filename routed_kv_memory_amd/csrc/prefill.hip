@@ -59,8 +59,8 @@ prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint
                const uint16_t* __restrict__ ctx_v, const int32_t* __restrict__ ctx_len, int32_t max_ctx,
                const uint16_t* __restrict__ loc_k, const uint16_t* __restrict__ loc_v,
                const int32_t* __restrict__ loc_len, int32_t max_loc, float scale, float* __restrict__ out) {
-  __shared__ uint16_t k_s[kKeyTile * kKStride];
-  __shared__ uint16_t v_s[kKeyTile * kVStride];
+  __shared__ uint16_t k_s[2][kKeyTile * kKStride];   // double buffered: one barrier per tile
+  __shared__ uint16_t v_s[2][kKeyTile * kVStride];
 
   constexpr int NT = 64 * G;
   const int t0 = blockIdx.x * kQBlock;
@@ -121,28 +121,38 @@ prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint
       pv[i] = vw;
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int u = tid + i * NT;
       if (u >= kKeyTile * 16) break;
       const int kk = u >> 4, c = u & 15;
-      *reinterpret_cast<uint4*>(k_s + kk * kKStride + c * 8) = pk[i];
-      *reinterpret_cast<uint4*>(v_s + kk * kVStride + c * 8) = pv[i];
+      *reinterpret_cast<uint4*>(k_s[buf] + kk * kKStride + c * 8) = pk[i];
+      *reinterpret_cast<uint4*>(v_s[buf] + kk * kVStride + c * 8) = pv[i];
     }
   };
 
+  // Scores are kept in log2 units (scale folded with log2 e).  The running maximum is
+  // raised only when a tile exceeds it by more than kSlack, so unnormalised
+  // probabilities stay below 2^kSlack and the accumulators are rescaled rarely.
+  constexpr float kSlack = 8.f;
+  const float scale2 = scale * 1.4426950408889634f;
   float m_run = ninf, l_lane = 0.f;
   f32x4 o[8];   // O^T: dims 16 dt + 4 g + r, token t0 + j
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (n_keys > 0) load_tile(0);
-  for (int32_t k0 = 0; k0 < n_keys; k0 += kKeyTile) {
-    __syncthreads();   // the previous tile's readers are done
-    store_tile();
-    __syncthreads();
+  // keys every token of the block may see: the first token's limit
+  const int32_t all_visible = clen + (t0 < T ? visible(t0) : 0);
+  if (n_keys > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  int buf = 0;
+  for (int32_t k0 = 0; k0 < n_keys; k0 += kKeyTile, buf ^= 1) {
+    __syncthreads();   // tile k0 is in buf; every reader of buf ^ 1 (the tile before) is done
     if (k0 + kKeyTile < n_keys) load_tile(k0 + kKeyTile);
+    const uint16_t* kt = k_s[buf];
 
     // S^T for keys k0 + 16 h2 + 4 g + r (h2 = 0, 1), token t0 + j
     f32x4 sc[2];
@@ -151,37 +161,55 @@ prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint
       sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 kw = *reinterpret_cast<const u32x4*>(k_s + (16 * h2 + j) * kKStride + 32 * s + 8 * g);
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(kt + (16 * h2 + j) * kKStride + 32 * s + 8 * g);
         sc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[s], sc[h2], 0, 0, 0);
       }
     }
-    // scale and mask
+    // scale to log2 units and mask (tiles every token of the block sees whole need no mask)
     float mt = ninf;
+    if (k0 + kKeyTile <= all_visible) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int32_t key = k0 + 16 * h2 + 4 * g + r;
-        const bool ok = key < n_keys && (key < clen || key - clen < vis_tok);
-        const float v = ok ? sc[h2][r] * scale : ninf;
-        sc[h2][r] = v;
-        mt = fmaxf(mt, v);
-      }
+        for (int r = 0; r < 4; ++r) {
+          sc[h2][r] *= scale2;
+          mt = fmaxf(mt, sc[h2][r]);
+        }
+    } else {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int32_t key = k0 + 16 * h2 + 4 * g + r;
+          const bool ok = key < n_keys && (key < clen || key - clen < vis_tok);
+          const float v = ok ? sc[h2][r] * scale2 : ninf;
+          sc[h2][r] = v;
+          mt = fmaxf(mt, v);
+        }
+    }
     mt = rows4_max(mt);                      // over the tile's 32 keys of token t0 + j
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == ninf ? 0.f : m_new;   // a token with no visible key yet
-    const float alpha = __expf(m_run - m_use);
+    // raise the reference maximum only past the slack (ballot: most tiles skip the rescale)
+    const bool raise = mt > m_run + kSlack;
+    float alpha = 1.f;
+    if (__ballot(raise)) {
+      const float m_new = raise ? mt : m_run;
+      alpha = m_run == ninf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_lane *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
+    const float m_use = m_run == ninf ? 0.f : m_run;   // a token with no visible key yet
     float psum = 0.f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = __expf(sc[h2][r] - m_use);
+        const float p = __builtin_amdgcn_exp2f(sc[h2][r] - m_use);
         sc[h2][r] = p;
         psum += p;
       }
-    l_lane = l_lane * alpha + psum;
-    m_run = m_new;
+    l_lane += psum;
     // P^T as the B operand: k slot 8 g + e holds key 4 g + e (e < 4) or 16 + 4 g + e - 4.
     // P = P_hi + P_lo with both parts in bf16 (two products), so the probabilities
     // enter the matrix cores with ~16 significant bits rather than 8.
@@ -197,16 +225,16 @@ prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint
     // V^T fragments by transposed reads of the row-major V tile: lane (g, j) of the
     // A operand needs dim 16 dt + j of keys 4 g + e and 16 + 4 g + e (e = 0..3), so
     // source lane j points at dims 16 dt + 4 (j & 3) .. +3 of key 4 g + (j >> 2).
-    const uint16_t* vsrc = v_s + (4 * g + (j >> 2)) * kVStride + 4 * (j & 3);
+    const uint16_t* vsrc = v_s[buf] + (4 * g + (j >> 2)) * kVStride + 4 * (j & 3);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const uint2 a0 = lds_read_tr16(vsrc + 16 * dt);
       const uint2 a1 = lds_read_tr16(vsrc + 16 * kVStride + 16 * dt);
       const u32x4 vw = {a0.x, a0.y, a1.x, a1.y};
-      o[dt] *= alpha;
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vw), pfh, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vw), pfl, o[dt], 0, 0, 0);
     }
+    if (k0 + kKeyTile < n_keys) store_tile(buf ^ 1);
   }
 
   const float l_tok = rows4_sum(l_lane);

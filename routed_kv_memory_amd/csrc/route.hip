@@ -88,8 +88,8 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 // contiguous eighth of the layer's items with no further synchronisation.
 //
 // Per tile a wave streams the 8 heads' 4 KiB key slices (four contiguous 1 KiB
-// fragments each) through a register ring, three slices ahead, with nontemporal
-// loads.  The same fragment bytes serve as the A operand (query: rows = tokens,
+// fragments each) through a register ring, three slices ahead (nontemporal loads
+// when no other workgroup re-reads the keys).  The same fragment bytes serve as the A operand (query: rows = tokens,
 // read from LDS) and the B operand (keys: columns = blocks) of
 // v_mfma_f32_16x16x32_bf16, so lane l ends up owning block (l & 15) and tokens
 // 4*(l >> 4) + r of each 16-token group.  Per head four more MFMAs of the key
@@ -131,7 +131,10 @@ __device__ __forceinline__ void emit_doc(uint32_t* __restrict__ codes, int32_t d
   else codes[doc] = ordered_code(v);
 }
 
-template <int NT>
+// STREAM: the keys are read once (one query chunk per range), so nontemporal loads
+// keep them from displacing other lines; with several query chunks the workgroups
+// sharing a range re-read each tile, and ordinary loads let L2 serve the repeats.
+template <int NT, bool STREAM>
 __global__ void __launch_bounds__(kScanWG)
 route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t n_tc,
                   const uint4* __restrict__ krt, int64_t tiles, const int32_t* __restrict__ blk_doc,
@@ -217,7 +220,8 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
       auto issue = [&](u32x4 (&kbuf)[4]) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          kbuf[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + s * 64));
+          kbuf[s] = STREAM ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + s * 64))
+                           : *reinterpret_cast<const u32x4*>(src + s * 64);
         if (unext + 1 < n_units) {
           ++unext;
           src += kHeadU4;
@@ -478,16 +482,17 @@ hipError_t launch_route_scores(int32_t L, const uint16_t* qr, int32_t B, int32_t
       const dim3 grid((unsigned)(R * C));
       const uint4* kt = reinterpret_cast<const uint4*>(krt);
       const int excl = (n_tc == 1 && !accumulate) ? 1 : 0;
+#define MSA_ROUTE_LAUNCH(NTV, ST)                                                                          \
+  hipLaunchKernelGGL((route_mfma_kernel<NTV, ST>), grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, tiles, blk_doc, \
+                     n_docs, L, R, excl, codes)
+      const bool stream = C == 1;
       switch (NT) {
-        case 1: hipLaunchKernelGGL(route_mfma_kernel<1>, grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, tiles,
-                                   blk_doc, n_docs, L, R, excl, codes); break;
-        case 2: hipLaunchKernelGGL(route_mfma_kernel<2>, grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, tiles,
-                                   blk_doc, n_docs, L, R, excl, codes); break;
-        case 3: hipLaunchKernelGGL(route_mfma_kernel<3>, grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, tiles,
-                                   blk_doc, n_docs, L, R, excl, codes); break;
-        default: hipLaunchKernelGGL(route_mfma_kernel<4>, grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, tiles,
-                                    blk_doc, n_docs, L, R, excl, codes); break;
+        case 1: if (stream) MSA_ROUTE_LAUNCH(1, true); else MSA_ROUTE_LAUNCH(1, false); break;
+        case 2: if (stream) MSA_ROUTE_LAUNCH(2, true); else MSA_ROUTE_LAUNCH(2, false); break;
+        case 3: if (stream) MSA_ROUTE_LAUNCH(3, true); else MSA_ROUTE_LAUNCH(3, false); break;
+        default: if (stream) MSA_ROUTE_LAUNCH(4, true); else MSA_ROUTE_LAUNCH(4, false); break;
       }
+#undef MSA_ROUTE_LAUNCH
     } else {
       const dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)B, (unsigned)L);
       hipLaunchKernelGGL(route_valu_kernel<16>, grid, dim3(256), 0, s, qr, B, T,
