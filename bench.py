@@ -34,8 +34,8 @@ POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 # WRITE_SIZE rocprofv3 passes (scaled by a 1 GiB calibration kernel) recorded in
 # profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
 # sources' digest differs, the figure is stale and bench.py reports null.
-SCAN_TRAFFIC_BYTES = 57.690e9
-SCAN_TRAFFIC_SOURCE_DIGEST = "f1f82a81ea3fbae1d31cdbe0363ea523cc920825be6a3d9eb1fa3f27436201b3"
+SCAN_TRAFFIC_BYTES = 57.692e9
+SCAN_TRAFFIC_SOURCE_DIGEST = "6dad12db310dcb54ad0048b548eb18836a8ddbf8d02ed88edf590d65177fe1df"
 
 
 def scan_source_digest():

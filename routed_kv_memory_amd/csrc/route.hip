@@ -205,13 +205,17 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
     }
     lds_barrier();
 
-    // this wave's contiguous share of the layer's items
+    // This wave's share of the layer's items: a contiguous eighth when the keys are
+    // streamed once; every eighth tile when several query chunks re-read the range,
+    // so that all waves of all those workgroups walk one front through L2.
     const int64_t n_items = seg_end - seg;
-    const int64_t w0 = seg + n_items * wave / kScanWaves;
-    const int64_t w1 = seg + n_items * (wave + 1) / kScanWaves;
-    if (w0 < w1) {
+    const int64_t w0 = STREAM ? seg + n_items * wave / kScanWaves : seg + wave;
+    const int64_t w1 = STREAM ? seg + n_items * (wave + 1) / kScanWaves : seg_end;
+    constexpr int64_t tstep = STREAM ? 1 : kScanWaves;
+    const int64_t n_tw = w0 < w1 ? (w1 - w0 + tstep - 1) / tstep : 0;   // tiles of this wave
+    if (n_tw > 0) {
       uint32_t* lcodes = codes + ((int64_t)layer * B + b) * n_docs;
-      const int64_t n_units = (w1 - w0) * kHeads;   // key slices of the run, consecutive in memory
+      const int64_t n_units = n_tw * kHeads;        // key slices of the wave's tiles
       const uint4* src = krt + w0 * kTileU4 + lane;
       int64_t unext = 0;
       u32x4 kb[kRing][4];
@@ -224,7 +228,7 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
                            : *reinterpret_cast<const u32x4*>(src + s * 64);
         if (unext + 1 < n_units) {
           ++unext;
-          src += kHeadU4;
+          src += (unext & (kHeads - 1)) == 0 ? (tstep - 1) * kTileU4 + kHeadU4 : kHeadU4;
         }
       };
 #pragma unroll
@@ -241,7 +245,7 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
       int32_t dcur = -1;
       f32x4 tot[NT];
 
-      for (int64_t ti = w0; ti < w1; ++ti) {
+      for (int64_t ti = 0; ti < n_tw; ++ti) {
 #pragma unroll
         for (int h = 0; h < kHeads; ++h) {
           // keeps each head's query-fragment reads from being hoisted into earlier heads
@@ -300,8 +304,9 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
             // document are contiguous, so a segmented suffix max within each run
             // of equal documents gives the run maxima; the last run stays open
             // because the document may continue in the next tile.
-            const bool t_first = tau == w0 - layer0;
-            const bool t_last = tau + 1 == w1 - layer0;
+            // with interleaved tiles every tile's edge runs may continue elsewhere
+            const bool t_first = !STREAM || ti == 0;
+            const bool t_last = !STREAM || ti + 1 == n_tw;
             int32_t d = -1;
             if (lane < kTile) {
               d = dcur;
@@ -349,7 +354,7 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
               if (cdoc >= 0 && lane == 0) emit_doc(lcodes, cdoc, cmax, true);
               cdoc = -1;
             }
-            ++tau;
+            tau += tstep;
           }
         }
       }
