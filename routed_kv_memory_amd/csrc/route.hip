@@ -443,16 +443,24 @@ route_valu_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, const u
 int choose_ranges(int C, int cus) {
   // R ranges per query chunk; the persistent grid of R*C workgroups (one per CU at a
   // time) should fill whole waves of the device: pick R in [ceil(cus/C), 4*ceil(cus/C)]
-  // with the best filled fraction, the smallest R on ties.
+  // with the best filled fraction.  When several query chunks share each range, a
+  // multiple of 8 wins ties, so that each range's workgroups sit on one XCD (one L2);
+  // otherwise the smallest R wins.
   if (C >= cus) return 1;
   const int r0 = (cus + C - 1) / C;
   int best = r0;
   double best_eff = 0.0;
+  bool best_x8 = false;
   for (int R = r0; R <= 4 * r0; ++R) {
     const long total = (long)R * C;
     const long waves = (total + cus - 1) / cus;
     const double eff = (double)total / (double)(waves * cus);
-    if (eff > best_eff + 1e-9) { best_eff = eff; best = R; }
+    const bool x8 = C > 1 && (R & 7) == 0;
+    if (eff > best_eff + 1e-9 || (eff > best_eff - 1e-9 && x8 && !best_x8)) {
+      best_eff = eff;
+      best = R;
+      best_x8 = x8;
+    }
   }
   return best;
 }
