@@ -51,9 +51,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="100m", choices=["tiny", "1m", "10m", "100m", "prefill", "interleaved"],
+    ap.add_argument("--workload", default="100m", choices=["tiny", "1m", "10m", "100m", "prefill", "interleaved", "host-tier"],
                     help="prefill: the multi-token sparse prefill alone at the interleaved workload's last "
                          "round (18 layers x 8 queries x 1,088 tokens); reported against the bf16 MFMA peak")
+    ap.add_argument("--host-groups", type=int, default=6,
+                    help="host-tier: layer groups whose top-k and host gather overlap the next group's scan")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -83,6 +85,8 @@ def main():
         return prefill_bench(args)
     if args.workload == "interleaved":
         return interleaved_bench(args)
+    if args.workload == "host-tier":
+        return host_tier_bench(args)
     cfg = S.CONFIGS[args.workload]
     L, B, T, k, Hq = cfg.n_layers, cfg.B, cfg.T, cfg.k, cfg.Hq
     t_setup = time.time()
@@ -264,6 +268,122 @@ def main():
         result["calibration_copy_bytes"] = 1 << 30
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, n_blk, blk.numpy(), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def host_tier_bench(args):
+    """The step with the content K-bar/V-bar in pinned host DRAM (the pages' own deployment):
+    routing keys stay in HBM, and each layer group's Top-16 documents are gathered over the host
+    link on a second stream while the next group's layers are scanned.  Pinned host memory on
+    this machine is capped near 64 GiB, so the 100M-token memory's 115 GB of content cannot be
+    pinned; the 10M-token memory (11.5 GB of content, the same document-length mix, 32 queries)
+    is used, and the link traffic is reported per query (it depends only on the selected
+    documents' lengths)."""
+    import numpy as np
+    import torch
+
+    from routed_kv_memory_amd import msa
+    from synth import synth as S
+    from synth.device import DeviceInputs
+
+    cfg = S.CONFIGS["10m"]
+    dev = "cuda"
+    L, B, k, Hq = cfg.n_layers, cfg.B, cfg.k, cfg.Hq
+    t_setup = time.time()
+    di = DeviceInputs(cfg, dev)
+    blk = di.prepooled_offsets()
+    n_blk = int(blk[-1])
+    max_db = int((blk[1:] - blk[:-1]).max())
+    n_docs = blk.numel() - 1
+    blk_d = blk.to(dev)
+    tiles = msa.msa_route_tiles(n_blk)
+    krt = torch.empty((L, tiles * 16, 8, 128), dtype=torch.bfloat16, device=dev)
+    for l, rows in di.prepooled_route_rows():
+        msa.msa_pack_route_keys(rows.view(1, n_blk, 8, 128), n_blk, krt[l:l + 1])
+    blk_doc = torch.empty(tiles * 16, dtype=torch.int32, device=dev)
+    msa.msa_block_doc_map(blk_d, n_blk, blk_doc)
+    kh, vh = di.prepooled_content_host()
+    qr = di.qr()
+    q, lk, lv, ll = di.decode_inputs()
+    max_ctx = k * max_db
+    dsc = torch.empty((L, B, n_docs), dtype=torch.float32, device=dev)
+    ids = torch.empty((L, B, k), dtype=torch.int32, device=dev)
+    tsc = torch.empty((L, B, k), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(msa.msa_topk_docs_workspace_size(L, B, n_docs, k), 256), dtype=torch.uint8, device=dev)
+    ck = torch.empty((L, B, max_ctx, 8, 128), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    cl = torch.empty((L, B), dtype=torch.int32, device=dev)
+    out = torch.empty((L, B, Hq, 128), dtype=torch.float32, device=dev)
+    ws_dec = torch.empty(msa.msa_sparse_decode_workspace_size(L, B, Hq, max_ctx, cfg.L_loc), dtype=torch.uint8,
+                         device=dev)
+    scale = 1.0 / math.sqrt(128.0)
+    torch.cuda.synchronize()
+    print("bench: host-tier memory ready in %.1f s (%.1f GB pinned host content)"
+          % (time.time() - t_setup, 2 * sum(t.numel() for t in kh) * 2 / 1e9), file=sys.stderr, flush=True)
+
+    def gather_layers(l0, l1, stream=None):
+        # the content is one pinned allocation per layer
+        for l in range(l0, l1):
+            msa.msa_gather_ctx(ids[l:l + 1], blk_d, max_db, kh[l], vh[l], ck[l:l + 1], cv[l:l + 1], cl[l:l + 1],
+                               stream=stream)
+
+    G = max(1, min(args.host_groups, L))
+    bounds = [L * g // G for g in range(G + 1)]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()            # default priority
+    evs = [torch.cuda.Event() for _ in range(G)]
+
+    def step(overlap=True):
+        for g in range(G):
+            l0, l1 = bounds[g], bounds[g + 1]
+            msa.msa_route_scores(qr[l0:l1], krt[l0:l1], n_blk, blk_doc, n_docs, dsc[l0:l1])
+            s = side if overlap else main
+            if overlap:
+                evs[g].record(main)
+                side.wait_event(evs[g])
+            msa.msa_topk_docs(dsc[l0:l1], k, ids[l0:l1], tsc[l0:l1], ws, stream=s)
+            gather_layers(l0, l1, stream=s)
+        if overlap:
+            main.wait_stream(side)
+        msa.msa_sparse_decode(q, ck, cv, cl, lk, lv, ll, scale, out, ws_dec)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n * 1e3
+
+    for _ in range(args.warmup):
+        step(True)
+        step(False)
+    ms_overlap = timed(lambda: step(True), args.steps)
+    ms_serial = timed(lambda: step(False), args.steps)
+    # the gather alone, from host DRAM and (for scale) from an HBM copy of the selected rows' source
+    ms_gather_host = timed(lambda: gather_layers(0, L), args.steps)
+    ctx_rows = int(cl.sum().item())
+    link_bytes = ctx_rows * 2 * 2048                  # K-bar and V-bar rows read over the link
+    nd = S.needle_docs(cfg)
+    ids_h = ids.cpu().numpy()
+    needle_ok = all(set(ids_h[l, b].tolist()) == set(nd[b].tolist()) for l in range(L) for b in range(nd.shape[0]))
+    result = {
+        "metric": "host-tier step ms (content K/V in host DRAM), 18 layers, 10M-token memory, 32 queries",
+        "value": round(ms_overlap, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_overlap, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "10M-token memory, routing keys in HBM (5.76 GB), content K-bar/V-bar in pinned "
+                               "host DRAM (11.5 GB), %d queries x 64 tokens, top-16, local 1,024" % B,
+                   "layer_groups": G},
+        "ms_serial_one_stream": round(ms_serial, 4),
+        "overlap_saving_ms": round(ms_serial - ms_overlap, 4),
+        "host_gather_ms_18_layers": round(ms_gather_host, 4),
+        "host_gather_MB": round(link_bytes / 1e6, 2),
+        "host_gather_MB_per_query": round(link_bytes / 1e6 / B, 2),
+        "host_gather_ms_per_query_equivalent": round(ms_gather_host / B, 4),
+        "host_link_GBps": round(link_bytes / (ms_gather_host * 1e-3) / 1e9, 2),
+        "needles_are_topk": needle_ok,
+    }
     print(json.dumps(result), flush=True)
 
 

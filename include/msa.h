@@ -12,6 +12,8 @@
  *  [P2] xuqi2024.github.io, "【MSA】突破100M Token 上下文：记忆稀疏注意力架构深度解析",
  *       3.3.2 (64-token blocks, Top-16), 5.2 (concatenation, varlen attention),
  *       5.3 (map_tensor_to_group_ids).
+ *  [P3] bi-chao.com, "把一亿 token 装进模型的“记忆”里：EverMind 开源 MSA 能干什么、不能干什么…",
+ *       3.3 (routing keys on the GPU, content K/V in host memory).
  *  [P5] xiaohongrsx.github.io, "MSA paper reading", 方法拆解 (8 KV heads x 128 dims,
  *       18 routed layers, fixed 64-token blocks per document, Top-16 by cosine) and
  *       推理全流程 (context = [Top-16 compressed KV ; local KV]; memory KV is fixed
@@ -21,7 +23,8 @@
  *  - Shapes are fixed at H = 8 KV heads, D = 128, 64-token blocks.  bf16 values
  *    travel as uint16_t bit patterns.  Layouts are layer-major and row-major; a
  *    "row" is [8 heads][128 dims] = 1024 bf16.
- *  - Pointers without a _host suffix are DEVICE pointers owned by the caller; the
+ *  - Pointers without a _host suffix are DEVICE pointers owned by the caller (the
+ *    one exception, content K/V in pinned host memory, is noted at msa_gather_ctx); the
  *    library never allocates, frees or keeps them.  Workspaces are caller-owned
  *    device memory of at least the size the matching *_workspace_size returns.
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls
@@ -203,7 +206,13 @@ int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
  *
  * max_doc_blocks is the caller's bound on blocks per document (from
  * msa_block_offsets_host); max_ctx < k * max_doc_blocks is MSA_ERR_SHAPE.  Rows that
- * would pass max_ctx (only if the bound was wrong) are dropped. */
+ * would pass max_ctx (only if the bound was wrong) are dropped.
+ *
+ * Host tier [P1 推理流水线; P3 3.3; P5 KV 缓存压缩 + Memory Parallel: the compressed
+ * content K/V may stay in host DRAM and only the selected documents' blocks cross to
+ * the GPU]: kbar and vbar may point to pinned host memory that the device can address
+ * (hipHostMalloc); the kernel then reads the selected rows over the host link while
+ * ctx_k/ctx_v stay in device memory. */
 int msa_gather_ctx(int32_t n_layers, int32_t B, const int32_t* topk_ids, int32_t k,
                    const int64_t* doc_blk_off, int32_t n_docs, int32_t max_doc_blocks,
                    const uint16_t* kbar, const uint16_t* vbar, int64_t n_blk,

@@ -80,7 +80,7 @@ def _check(fn: str, status: int):
         raise MsaError(fn, status, lib().msa_last_error().decode(errors="replace"))
 
 
-def _ptr(t, dtypes, name, allow_none=False):
+def _ptr(t, dtypes, name, allow_none=False, allow_pinned=False):
     if t is None:
         if allow_none:
             return None
@@ -91,8 +91,8 @@ def _ptr(t, dtypes, name, allow_none=False):
         raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
-    if not t.is_cuda:
-        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_cuda and not (allow_pinned and t.is_pinned()):
+        raise ValueError("%s must be a GPU tensor%s" % (name, " or pinned host memory" if allow_pinned else ""))
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -203,13 +203,15 @@ def msa_route_topk(qr, krbar_route, n_blk, blk_doc, n_docs, k, topk_ids, topk_sc
 
 
 def msa_gather_ctx(topk_ids, doc_blk_off, max_doc_blocks, kbar, vbar, ctx_k, ctx_v, ctx_len, stream=None):
+    """kbar/vbar may live in HBM or in pinned host memory (read over the host link)."""
     L, B, k = topk_ids.shape
     n_docs = doc_blk_off.numel() - 1
     n_blk = kbar.shape[1]
     max_ctx = ctx_k.shape[2]
     _check("msa_gather_ctx", lib().msa_gather_ctx(
         L, B, _ptr(topk_ids, _I32T, "topk_ids"), k, _ptr(doc_blk_off, _I64T, "doc_blk_off"), n_docs,
-        max_doc_blocks, _ptr(kbar, _BF16, "kbar"), _ptr(vbar, _BF16, "vbar"), n_blk, max_ctx,
+        max_doc_blocks, _ptr(kbar, _BF16, "kbar", allow_pinned=True), _ptr(vbar, _BF16, "vbar", allow_pinned=True),
+        n_blk, max_ctx,
         _ptr(ctx_k, _BF16, "ctx_k"), _ptr(ctx_v, _BF16, "ctx_v"), _ptr(ctx_len, _I32T, "ctx_len"),
         _stream(stream)))
 

@@ -75,6 +75,23 @@ class DeviceInputs:
             out.append(t)
         return out[0], out[1]
 
+    def prepooled_content_host(self):
+        """The same K-bar, V-bar as prepooled_content, in pinned host memory: two lists of
+        per-layer [N_blk][8][128] tensors (generated on the device one layer at a time)."""
+        mem = self.mem
+        per = mem.n_blk * S.H * S.D
+        stage = torch.empty((mem.n_blk, S.H, S.D), dtype=torch.bfloat16, device=self.device)
+        out = []
+        for stream in (S.S_KBAR, S.S_VBAR):
+            layers = []
+            for l in range(mem.n_layers):
+                h = torch.empty((1, mem.n_blk, S.H, S.D), dtype=torch.bfloat16, pin_memory=True)
+                self.gen.fill(stage, mem.seed, stream, l * per)
+                h[0].copy_(stage)
+                layers.append(h)
+            out.append(layers)
+        return out[0], out[1]
+
     def prepooled_route_rows(self, staging: torch.Tensor = None):
         """Yields (layer, rows [N_blk][8][128] bf16) of the row-major routing keys, needles
         planted, one layer at a time in a reused staging buffer."""
