@@ -258,3 +258,76 @@ void orc_prefill(int32_t T, int32_t Hq, const uint16_t* q,
                    out + (size_t)t * Hq * ORC_D);
     }
 }
+
+/* ----------------------------------------------------------------- encode */
+
+void orc_encode(int32_t H, const uint16_t* x, int64_t n_tok,
+                const uint16_t* w_k, const uint16_t* w_v, const uint16_t* w_kr, const uint16_t* w_norm,
+                double eps, double theta,
+                const int64_t* doc_tok_off, const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk,
+                uint16_t* kbar, uint16_t* vbar, uint16_t* krbar)
+{
+    double* k = (double*)malloc(ORC_ROW * sizeof(double));
+    double* v = (double*)malloc(ORC_ROW * sizeof(double));
+    double* r = (double*)malloc(ORC_ROW * sizeof(double));
+    double* sk = (double*)malloc(ORC_ROW * sizeof(double));
+    double* sv = (double*)malloc(ORC_ROW * sizeof(double));
+    double* sr = (double*)malloc(ORC_ROW * sizeof(double));
+    (void)n_tok;
+    (void)n_blk;
+    for (int32_t d = 0; d < n_docs; ++d) {
+        int64_t s = doc_tok_off[d], e = doc_tok_off[d + 1];
+        for (int64_t j = 0; doc_blk_off[d] + j < doc_blk_off[d + 1]; ++j) {
+            int64_t t0 = s + ORC_BLOCK * j;
+            int64_t t1 = t0 + ORC_BLOCK < e ? t0 + ORC_BLOCK : e;
+            for (int c = 0; c < ORC_ROW; ++c) sk[c] = sv[c] = sr[c] = 0.0;
+            for (int64_t t = t0; t < t1; ++t) {
+                const uint16_t* xt = x + (size_t)t * H;
+                /* the three projections */
+                for (int c = 0; c < ORC_ROW; ++c) k[c] = v[c] = r[c] = 0.0;
+                for (int32_t i = 0; i < H; ++i) {
+                    double xi = orc_bf16_to_double(xt[i]);
+                    if (xi == 0.0) continue;
+                    const uint16_t* wk = w_k + (size_t)i * ORC_ROW;
+                    const uint16_t* wv = w_v + (size_t)i * ORC_ROW;
+                    const uint16_t* wr = w_kr + (size_t)i * ORC_ROW;
+                    for (int c = 0; c < ORC_ROW; ++c) {
+                        k[c] += xi * orc_bf16_to_double(wk[c]);
+                        v[c] += xi * orc_bf16_to_double(wv[c]);
+                        r[c] += xi * orc_bf16_to_double(wr[c]);
+                    }
+                }
+                /* key: per-head RMS normalisation, then the document-wise rotation */
+                double p = (double)(t - s);
+                for (int h = 0; h < ORC_H; ++h) {
+                    double* kh = k + h * ORC_D;
+                    double ms = 0.0;
+                    for (int i = 0; i < ORC_D; ++i) ms += kh[i] * kh[i];
+                    double inv = 1.0 / sqrt(ms / ORC_D + eps);
+                    for (int i = 0; i < ORC_D; ++i) kh[i] *= inv * orc_bf16_to_double(w_norm[i]);
+                    for (int i = 0; i < ORC_D / 2; ++i) {
+                        double ang = p * pow(theta, -(double)i / (ORC_D / 2));
+                        double c0 = cos(ang), s0 = sin(ang);
+                        double a = kh[i], b = kh[i + ORC_D / 2];
+                        kh[i] = a * c0 - b * s0;
+                        kh[i + ORC_D / 2] = b * c0 + a * s0;
+                    }
+                }
+                for (int c = 0; c < ORC_ROW; ++c) {
+                    sk[c] += k[c];
+                    sv[c] += v[c];
+                    sr[c] += r[c];
+                }
+            }
+            size_t o = (size_t)(doc_blk_off[d] + j) * ORC_ROW;
+            double n = (double)(t1 - t0);
+            for (int c = 0; c < ORC_ROW; ++c) {
+                kbar[o + c] = orc_bf16_from_double(sk[c] / n);
+                vbar[o + c] = orc_bf16_from_double(sv[c] / n);
+                krbar[o + c] = orc_bf16_from_double(sr[c] / n);
+            }
+        }
+    }
+    free(k); free(v); free(r); free(sk); free(sv); free(sr);
+}
+

@@ -35,6 +35,8 @@
  *   orc_decode                                  pinned (single key, equal keys, q=0, library softmax, permutation)
  *   orc_prefill                                 pinned (library masked attention, T = 1 is decode, causality,
  *                                               single visible row)
+ *   orc_encode                                  pinned (identity projection = orc_pool, library matmul, unit
+ *                                               RMS, RoPE angle and pair norm per position, document order)
  */
 #ifndef MSA_ORACLE_H
 #define MSA_ORACLE_H
@@ -129,6 +131,25 @@ void orc_prefill(int32_t T, int32_t Hq, const uint16_t* q,
                  const uint16_t* ctx_k, const uint16_t* ctx_v, int64_t n_ctx,
                  const uint16_t* loc_k, const uint16_t* loc_v, int64_t n_loc,
                  double scale, double* out);
+
+/* [P2 5.2 Step 1 (k_proj, k_norm, v_proj); P2 5.1 (router_k_proj, a bias-free
+ * linear map to 8 x 128); P2 3.3.1 and P1 整体设计 -> 架构 (parallel, document-wise
+ * RoPE: positions restart at 0 in every document); then the block pooling of
+ * orc_pool]  The offline encode of one layer's memory documents.  For token t at
+ * position p (its offset inside its document), with hidden row x_t of length H:
+ *   k = x_t W_k, normalised per head by its root mean square (+ eps) and scaled by
+ *   w_norm, then rotated: for e < 64, angle = p * theta^(-e/64),
+ *   k'[e] = k[e] cos - k[e+64] sin,  k'[e+64] = k[e+64] cos + k[e] sin  (per head);
+ *   v = x_t W_v;  kr = x_t W_kr  (no norm, no rotation).
+ * Each is then mean-pooled over the document's 64-token blocks as in orc_pool and
+ * rounded once to bf16.  fp64 throughout.
+ * x: [n_tok][H]; W_*: [H][8 * 128] (input-major); w_norm: [128];
+ * kbar, vbar, krbar: [n_blk][8][128]. */
+void orc_encode(int32_t H, const uint16_t* x, int64_t n_tok,
+                const uint16_t* w_k, const uint16_t* w_v, const uint16_t* w_kr, const uint16_t* w_norm,
+                double eps, double theta,
+                const int64_t* doc_tok_off, const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk,
+                uint16_t* kbar, uint16_t* vbar, uint16_t* krbar);
 
 #ifdef __cplusplus
 }

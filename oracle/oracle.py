@@ -61,6 +61,7 @@ def lib():
         L.orc_gather.restype = i64
         L.orc_decode.argtypes = [i32, P, P, P, i64, P, P, i64, f64, P]
         L.orc_prefill.argtypes = [i32, i32, P, P, P, i64, P, P, i64, f64, P]
+        L.orc_encode.argtypes = [i32, P, i64, P, P, P, P, f64, f64, P, P, i32, i64, P, P, P]
         _lib = L
     return _lib
 
@@ -233,6 +234,20 @@ def prefill(q, ctx_k, ctx_v, loc_k, loc_v, scale: float) -> np.ndarray:
     return out
 
 
+def encode(x, w_k, w_v, w_kr, w_norm, eps: float, theta: float, doc_tok_off, doc_blk_off):
+    """One layer: x [n_tok][H]; W_* [H][8*128]; w_norm [128] -> pooled (kbar, vbar, krbar) [n_blk][8][128]."""
+    x = _u16(x)
+    n_tok, Hd = x.shape
+    wk, wv, wr, wn = _u16(w_k), _u16(w_v), _u16(w_kr), _u16(w_norm)
+    assert wk.shape == (Hd, ROW) and wv.shape == (Hd, ROW) and wr.shape == (Hd, ROW) and wn.size == D
+    t, b = _i64(doc_tok_off), _i64(doc_blk_off)
+    n_docs, n_blk = t.size - 1, int(b[-1])
+    outs = [np.zeros((max(n_blk, 1), H, D), np.uint16) for _ in range(3)]
+    lib().orc_encode(Hd, _p(x), n_tok, _p(wk), _p(wv), _p(wr), _p(wn), float(eps), float(theta), _p(t), _p(b),
+                     n_docs, n_blk, _p(outs[0]), _p(outs[1]), _p(outs[2]))
+    return tuple(o[:n_blk] for o in outs)
+
+
 __all__ = ["build", "lib", "bf16_to_f64", "bf16_from_f64", "bf16_from_f64_scalar", "group_ids",
            "doc_tok_offsets", "block_offsets", "pool", "head_norms", "block_score", "doc_scores",
-           "doc_scores_all", "topk", "gather", "decode", "prefill", "H", "D", "BLOCK", "ROW"]
+           "doc_scores_all", "topk", "gather", "decode", "prefill", "encode", "H", "D", "BLOCK", "ROW"]

@@ -460,3 +460,103 @@ def test_prefill_first_token_of_a_bare_query_sees_one_row(orc):
     out = orc.prefill(q, ck, cv, lk, lv, 0.1)
     for hq in range(32):
         assert np.array_equal(out[0, hq], val(lv[0, hq // 4]))
+
+
+# -------------------------------------------------------------------- encode
+
+def _eye_bf16(n):
+    w = np.zeros((n, ROW), np.uint16)
+    w[np.arange(n), np.arange(n)] = bf([1.0])[0]
+    return w
+
+
+def _offsets(lens):
+    tok = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    blk = np.concatenate([[0], np.cumsum((np.asarray(lens) + 63) // 64)]).astype(np.int64)
+    return tok, blk
+
+
+def test_encode_identity_projection_is_the_block_pooling(orc):
+    """With W_v = W_kr = I (H = 1024) the encode pools the hidden rows themselves."""
+    rng = np.random.default_rng(50)
+    lens = [1, 64, 65, 130, 7]
+    tok, blk = _offsets(lens)
+    x = rand_bf16(rng, (int(tok[-1]), ROW))
+    eye = _eye_bf16(ROW)
+    _, vbar, krbar = orc.encode(x, eye, eye, eye, np.full(D, bf([1.0])[0], np.uint16), 1e-6, 1e6, tok, blk)
+    ref = orc.pool(x.reshape(1, -1, H, D), tok, blk)[0]
+    assert np.array_equal(vbar, ref) and np.array_equal(krbar, ref)
+
+
+def test_encode_projection_matches_library_matmul(orc):
+    """Single-token documents: each pooled V / Kr row is bf16(x W) of numpy's fp64 matmul."""
+    rng = np.random.default_rng(51)
+    Hd, n = 96, 12
+    x = rand_bf16(rng, (n, Hd))
+    wk, wv, wr = (rand_bf16(rng, (Hd, ROW), 0.1) for _ in range(3))
+    tok, blk = _offsets([1] * n)
+    _, vbar, krbar = orc.encode(x, wk, wv, wr, np.full(D, bf([1.0])[0], np.uint16), 1e-6, 1e6, tok, blk)
+    for w, got in ((wv, vbar), (wr, krbar)):
+        ref = orc.bf16_from_f64(val(x) @ val(w)).reshape(n, H, D)
+        d = np.abs(ref.astype(np.int32) - got.astype(np.int32))
+        assert d.max() <= 1 and (d > 0).mean() < 0.01       # fp64 summation order only
+
+
+def test_encode_key_is_rms_normalised_per_head(orc):
+    """Position 0 (no rotation) and unit norm weight: every head of every key has RMS 1."""
+    rng = np.random.default_rng(52)
+    Hd, n = 64, 10
+    x = rand_bf16(rng, (n, Hd))
+    wk = rand_bf16(rng, (Hd, ROW), 0.3)
+    tok, blk = _offsets([1] * n)
+    kbar, _, _ = orc.encode(x, wk, wk, wk, np.full(D, bf([1.0])[0], np.uint16), 1e-12, 1e6, tok, blk)
+    rms = np.sqrt((val(kbar) ** 2).mean(axis=-1))
+    assert np.allclose(rms, 1.0, atol=2.0 ** -8)
+    raw = (val(x) @ val(wk)).reshape(n, H, D)
+    ref = orc.bf16_from_f64(raw / np.sqrt((raw ** 2).mean(axis=-1, keepdims=True) + 1e-12))
+    assert np.abs(ref.astype(np.int32) - kbar.astype(np.int32)).max() <= 1
+
+
+def test_encode_rotation_angle_and_pair_norm_at_position_64(orc):
+    """The same hidden row at position 64 (the lone token of a 65-token document's second
+    block) and at position 0 (a 1-token document): every pair (e, e + 64) of every head keeps
+    its length and turns by 64 * theta^(-e/64)."""
+    rng = np.random.default_rng(53)
+    Hd, theta = 64, 10000.0
+    xr = rand_bf16(rng, (1, Hd))
+    x = np.concatenate([rand_bf16(rng, (64, Hd)), xr, xr])
+    wk = rand_bf16(rng, (Hd, ROW), 0.3)
+    tok, blk = _offsets([65, 1])
+    kbar, _, _ = orc.encode(x, wk, wk, wk, np.full(D, bf([1.0])[0], np.uint16), 1e-6, theta, tok, blk)
+    a, b = val(kbar[1]), val(kbar[2])          # position 64 / position 0
+    for h in range(H):
+        for e in range(D // 2):
+            ra, rb = np.hypot(a[h, e], a[h, e + 64]), np.hypot(b[h, e], b[h, e + 64])
+            assert abs(ra - rb) <= 2.0 ** -7 * max(rb, 1e-3) + 2.0 ** -10
+            if rb > 0.2:
+                turn = math.atan2(a[h, e + 64], a[h, e]) - math.atan2(b[h, e + 64], b[h, e])
+                want = 64.0 * theta ** (-e / 64.0)
+                err = (turn - want + math.pi) % (2 * math.pi) - math.pi
+                assert abs(err) < 0.03, (h, e, err)
+
+
+def test_encode_documents_are_position_independent_and_norm_weight_scales_keys(orc):
+    """Positions restart in every document: swapping two documents swaps their pooled rows
+    exactly; a norm weight of 2 doubles the keys exactly and leaves V and Kr alone."""
+    rng = np.random.default_rng(54)
+    Hd = 64
+    la, lb = 70, 130
+    xa, xb = rand_bf16(rng, (la, Hd)), rand_bf16(rng, (lb, Hd))
+    wk, wv, wr = (rand_bf16(rng, (Hd, ROW), 0.2) for _ in range(3))
+    one = np.full(D, bf([1.0])[0], np.uint16)
+    tok, blk = _offsets([la, lb])
+    ab = orc.encode(np.concatenate([xa, xb]), wk, wv, wr, one, 1e-6, 1e6, tok, blk)
+    tok2, blk2 = _offsets([lb, la])
+    ba = orc.encode(np.concatenate([xb, xa]), wk, wv, wr, one, 1e-6, 1e6, tok2, blk2)
+    na = (la + 63) // 64
+    for u, w in zip(ab, ba):
+        assert np.array_equal(u[:na], w[-na:]) and np.array_equal(u[na:], w[:-na])
+    two = orc.encode(np.concatenate([xa, xb]), wk, wv, wr, np.full(D, bf([2.0])[0], np.uint16), 1e-6, 1e6,
+                     tok, blk)
+    assert np.array_equal(val(two[0]), 2.0 * val(ab[0]))
+    assert np.array_equal(two[1], ab[1]) and np.array_equal(two[2], ab[2])
