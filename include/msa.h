@@ -244,6 +244,34 @@ int msa_sparse_decode(int32_t n_layers, int32_t B, int32_t Hq, const uint16_t* q
                       int32_t max_loc, float scale, float* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ offline encode front-end
+ *
+ * [P2 5.1 (router_k_proj: bias-free linear map to 8 x 128), 5.2 Step 1 (k_proj then
+ * k_norm, v_proj, rotary positions), 3.3.1 (document-wise positions restarting at 0);
+ * P1 整体设计 -> 架构]  For every memory token t at position p (its offset in its
+ * document) with hidden row x_t:  k = x_t W_k, scaled per head by 1/sqrt(mean(k^2) +
+ * eps) and by w_norm, then rotated (pairs (e, e + 64) of each head by the angle
+ * p * theta^(-e/64));  v = x_t W_v;  kr = x_t W_kr.  The three are mean-pooled over
+ * the document's 64-token blocks as msa_pool_blocks does (fp32, one rounding to bf16)
+ * without ever being stored per token.
+ *
+ *   x            [n_layers][n_tok][H] bf16, H a multiple of 32
+ *   w_k, w_v, w_kr [n_layers][H][8 * 128] bf16 (input-major: row i maps hidden dim i)
+ *   w_norm       [n_layers][128] bf16
+ *   doc_tok_off, doc_blk_off, n_docs, n_blk: as for msa_pool_blocks
+ *   kbar, vbar   [n_layers][n_blk][8][128] bf16 outputs
+ *   krbar_route  [n_layers][tiles * 16][8][128] bf16 output (route-key tile layout)
+ *   krbar_norm   [n_layers][tiles][8][16] fp32 output or NULL
+ *
+ * Errors: NULL pointers, sizes < 1, H % 32 != 0 (SHAPE); n_layers > 65535
+ * (UNSUPPORTED). */
+int msa_encode_blocks(int32_t n_layers, int32_t H, const uint16_t* x, int64_t n_tok,
+                      const uint16_t* w_k, const uint16_t* w_v, const uint16_t* w_kr,
+                      const uint16_t* w_norm, float eps, float theta,
+                      const int64_t* doc_tok_off, const int64_t* doc_blk_off, int32_t n_docs,
+                      int64_t n_blk, uint16_t* kbar, uint16_t* vbar, uint16_t* krbar_route,
+                      float* krbar_norm, void* stream);
+
 /* ------------------------------------------------------------ multi-token prefill
  *
  * [P2 5.2 (varlen attention over the query states and the concatenation of local and

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["abi.cpp", "pool.hip", "route.hip", "topk.hip", "gather.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["abi.cpp", "pool.hip", "route.hip", "topk.hip", "gather.hip", "decode.hip", "prefill.hip", "encode.hip"]
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden", "--offload-arch=" + ARCH,
          # packed fp32 VALU forms are kept out of generated code
@@ -29,7 +29,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 7)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = ["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs

@@ -283,6 +283,23 @@ MSA_API int msa_sparse_decode(int32_t n_layers, int32_t B, int32_t Hq, const uin
                     "msa_sparse_decode");
 }
 
+MSA_API int msa_encode_blocks(int32_t n_layers, int32_t H, const uint16_t* x, int64_t n_tok, const uint16_t* w_k,
+                              const uint16_t* w_v, const uint16_t* w_kr, const uint16_t* w_norm, float eps, float theta,
+                              const int64_t* doc_tok_off, const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk,
+                              uint16_t* kbar, uint16_t* vbar, uint16_t* krbar_route, float* krbar_norm, void* stream) {
+  if (!x || !w_k || !w_v || !w_kr || !w_norm || !doc_tok_off || !doc_blk_off || !kbar || !vbar || !krbar_route)
+    return fail(MSA_ERR_NULL, "msa_encode_blocks: null pointer");
+  if (n_layers < 1 || H < 32 || H % 32 != 0 || n_tok < 1 || n_docs < 1 || n_blk < 0 || !(eps >= 0.f) ||
+      !(theta > 0.f))
+    return fail(MSA_ERR_SHAPE, "msa_encode_blocks: n_layers=%d H=%d n_tok=%lld n_docs=%d n_blk=%lld", n_layers, H,
+                (long long)n_tok, n_docs, (long long)n_blk);
+  if (n_layers > 65535) return fail(MSA_ERR_UNSUPPORTED, "msa_encode_blocks: n_layers > 65535");
+  return hip_status(msa::launch_encode(n_layers, H, x, n_tok, w_k, w_v, w_kr, w_norm, eps, theta, doc_tok_off,
+                                       doc_blk_off, n_docs, n_blk, kbar, vbar, krbar_route, krbar_norm,
+                                       as_stream(stream)),
+                    "msa_encode_blocks");
+}
+
 MSA_API int msa_sparse_prefill(int32_t n_layers, int32_t B, int32_t T, int32_t Hq, const uint16_t* q,
                                const uint16_t* ctx_k, const uint16_t* ctx_v, const int32_t* ctx_len, int32_t max_ctx,
                                const uint16_t* loc_k, const uint16_t* loc_v, const int32_t* loc_len, int32_t max_loc,

@@ -43,6 +43,10 @@ hipError_t launch_decode(int32_t L, int32_t B, int32_t Hq, const uint16_t* q, co
                          const uint16_t* ctx_v, const int32_t* ctx_len, int32_t max_ctx, const uint16_t* loc_k,
                          const uint16_t* loc_v, const int32_t* loc_len, int32_t max_loc, float scale, float* out,
                          void* ws, hipStream_t s);
+hipError_t launch_encode(int32_t L, int32_t H, const uint16_t* x, int64_t n_tok, const uint16_t* w_k,
+                         const uint16_t* w_v, const uint16_t* w_kr, const uint16_t* w_norm, float eps, float theta,
+                         const int64_t* doc_tok_off, const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk,
+                         uint16_t* kbar, uint16_t* vbar, uint16_t* krt, float* krn, hipStream_t s);
 hipError_t launch_prefill(int32_t L, int32_t B, int32_t T, int32_t Hq, const uint16_t* q, const uint16_t* ctx_k,
                           const uint16_t* ctx_v, const int32_t* ctx_len, int32_t max_ctx, const uint16_t* loc_k,
                           const uint16_t* loc_v, const int32_t* loc_len, int32_t max_loc, float scale, float* out,

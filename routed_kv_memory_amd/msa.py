@@ -46,6 +46,8 @@ _SIGS = {
     "msa_sparse_decode_workspace_size": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_decode": ([_I32, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _F32, _P, _P, _SZ, _P],
                           ctypes.c_int),
+    "msa_encode_blocks": ([_I32, _I32, _P, _I64, _P, _P, _P, _P, _F32, _F32, _P, _P, _I32, _I64, _P, _P, _P, _P, _P],
+                          ctypes.c_int),
     "msa_sparse_prefill": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _F32, _P, _P],
                            ctypes.c_int),
 }
@@ -240,4 +242,17 @@ def msa_sparse_prefill(q, ctx_k, ctx_v, ctx_len, loc_k, loc_v, loc_len, scale, o
         L, B, T, Hq, _ptr(q, _BF16, "q"), _ptr(ctx_k, _BF16, "ctx_k"), _ptr(ctx_v, _BF16, "ctx_v"),
         _ptr(ctx_len, _I32T, "ctx_len"), ctx_k.shape[2], _ptr(loc_k, _BF16, "loc_k"), _ptr(loc_v, _BF16, "loc_v"),
         _ptr(loc_len, _I32T, "loc_len"), loc_k.shape[2], float(scale), _ptr(out, _F32T, "out"), _stream(stream)))
+
+
+def msa_encode_blocks(x, w_k, w_v, w_kr, w_norm, eps, theta, doc_tok_off, doc_blk_off, n_blk, kbar, vbar,
+                      krbar_route, krbar_norm=None, stream=None):
+    """x [L][n_tok][H]; W_* [L][H][1024]; w_norm [L][128]; outputs as msa_pool_blocks."""
+    L, n_tok, H = x.shape
+    n_docs = doc_tok_off.numel() - 1
+    _check("msa_encode_blocks", lib().msa_encode_blocks(
+        L, H, _ptr(x, _BF16, "x"), n_tok, _ptr(w_k, _BF16, "w_k"), _ptr(w_v, _BF16, "w_v"),
+        _ptr(w_kr, _BF16, "w_kr"), _ptr(w_norm, _BF16, "w_norm"), float(eps), float(theta),
+        _ptr(doc_tok_off, _I64T, "doc_tok_off"), _ptr(doc_blk_off, _I64T, "doc_blk_off"), n_docs, n_blk,
+        _ptr(kbar, _BF16, "kbar"), _ptr(vbar, _BF16, "vbar"), _ptr(krbar_route, _BF16, "krbar_route"),
+        _ptr(krbar_norm, _F32T, "krbar_norm", allow_none=True), _stream(stream)))
 

@@ -98,6 +98,16 @@ def test_invalid_arguments_are_rejected_on_the_host(msa):
                                   fake, None) == 2
     assert lib.msa_sparse_prefill(1, 1, 4, 24, fake, fake, fake, fake, 8, fake, fake, fake, 4, ctypes.c_float(0.1),
                                   fake, None) == 3
+    # encode: null, hidden size not a multiple of 32, zero layers
+    F = ctypes.c_float
+    assert lib.msa_encode_blocks(1, 64, None, 10, fake, fake, fake, fake, F(1e-6), F(1e6), fake, fake, 1, 1, fake,
+                                 fake, fake, None, None) == 1
+    assert lib.msa_encode_blocks(1, 48, fake, 10, fake, fake, fake, fake, F(1e-6), F(1e6), fake, fake, 1, 1, fake,
+                                 fake, fake, None, None) == 2
+    assert lib.msa_encode_blocks(0, 64, fake, 10, fake, fake, fake, fake, F(1e-6), F(1e6), fake, fake, 1, 1, fake,
+                                 fake, fake, None, None) == 2
+    assert lib.msa_encode_blocks(1, 64, fake, 10, fake, fake, fake, fake, F(1e-6), F(0.0), fake, fake, 1, 1, fake,
+                                 fake, fake, None, None) == 2
     # workspace too small
     need = lib.msa_route_topk_workspace_size(2, 1, 100000, 16)
     assert lib.msa_route_topk(2, fake, 1, 8, fake, 1000, fake, 100000, 16, fake, None, None, fake, need - 1,
