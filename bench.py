@@ -51,9 +51,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="100m", choices=["tiny", "1m", "10m", "100m", "prefill", "interleaved", "host-tier"],
+    ap.add_argument("--workload", default="100m", choices=["tiny", "1m", "10m", "100m", "prefill", "interleaved", "host-tier", "encode"],
                     help="prefill: the multi-token sparse prefill alone at the interleaved workload's last "
-                         "round (18 layers x 8 queries x 1,088 tokens); reported against the bf16 MFMA peak")
+                         "round (18 layers x 8 queries x 1,088 tokens); encode: the offline encode front-end "
+                         "over the 1M-token document set (18 layers, hidden 2,560); both reported against the "
+                         "bf16 MFMA peak")
     ap.add_argument("--host-groups", type=int, default=6,
                     help="host-tier: layer groups whose top-k and host gather overlap the next group's scan")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU-baseline sample")
@@ -87,6 +89,8 @@ def main():
         return interleaved_bench(args)
     if args.workload == "host-tier":
         return host_tier_bench(args)
+    if args.workload == "encode":
+        return encode_bench(args)
     cfg = S.CONFIGS[args.workload]
     L, B, T, k, Hq = cfg.n_layers, cfg.B, cfg.T, cfg.k, cfg.Hq
     t_setup = time.time()
@@ -560,6 +564,114 @@ def prefill_bench(args):
                                   "kind": "oracle",
                                   "sample": "fp64 oracle, last token of (layer 0, query 0): %d query heads over %d + "
                                             "%d rows, %d repetitions, %.2f s each" % (Hq, n_ctx, T, reps, dt)}
+    print(json.dumps(result), flush=True)
+
+
+def encode_bench(args):
+    """The offline encode front-end over the 1M-token document set: every layer projects its
+    hidden rows to K, V and Kr (8 heads x 128), normalises and rotates K, and pools the three
+    into 64-token block means, in one launch for all 18 layers."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from routed_kv_memory_amd import msa
+    from synth import synth as S
+    from synth.device import DeviceInputs
+
+    cfg = S.CONFIGS["1m"]
+    Hd, eps, theta = S.ENC_HIDDEN, 1e-6, 1e6
+    tok, x, wk, wv, wr, wn = DeviceInputs(cfg, "cuda").encode_inputs(Hd)
+    L, n_tok = x.shape[0], x.shape[1]
+    blk, n_blk, _ = msa.msa_block_offsets_host(tok)
+    tok_d, blk_d = tok.to("cuda"), blk.to("cuda")
+    kbar = torch.empty((L, n_blk, 8, 128), dtype=torch.bfloat16, device="cuda")
+    vbar = torch.empty_like(kbar)
+    tiles = msa.msa_route_tiles(n_blk)
+    krt = torch.empty((L, tiles * 16, 8, 128), dtype=torch.bfloat16, device="cuda")
+    krn = torch.empty((L, tiles * 16, 8), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    print("bench: encode inputs ready (%d layers x %d tokens x %d hidden, %d blocks, %.1f GB on device)"
+          % (L, n_tok, Hd, n_blk, torch.cuda.memory_allocated() / 1e9), file=sys.stderr, flush=True)
+
+    def step():
+        msa.msa_encode_blocks(x, wk, wv, wr, wn, eps, theta, tok_d, blk_d, n_blk, kbar, vbar, krt, krn)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    flop = 2.0 * L * n_tok * Hd * 3 * 1024                    # the three projections; the epilogue is O(n_tok)
+    tflops = flop / (wall / args.steps) / 1e12
+    achieved = flop / (ms * 1e-3) / 1e12
+    # algorithmic bytes: hidden rows and weights read once, pooled outputs written once
+    nbytes = L * (n_tok * Hd * 2 + 3 * Hd * 1024 * 2 + 3 * n_blk * 1024 * 2 + tiles * 16 * 8 * 4)
+
+    # sampled parity: V and Kr of blocks anywhere (no position dependence), K of documents'
+    # first blocks, against the oracle on the host-regenerated inputs
+    tok_n, blk_n = tok.numpy(), blk.numpy()
+    lens = np.diff(tok_n)
+    rng = np.random.default_rng(7)
+    samples = [(0, int(rng.integers(0, lens.size))), (L - 1, int(rng.integers(0, lens.size)))]
+    u16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    wn_h = u16(wn)
+    worst = 0.0
+    cpu_dt = []
+    for l, d in samples:
+        w_h = [np.ascontiguousarray(S.enc_weights_host(S.memory_config(cfg).seed, st, l, Hd).T)
+               for st in (S.S_ENC_WK, S.S_ENC_WV, S.S_ENC_WKR)]   # the oracle takes W as [hidden][1024]
+        jb = int(rng.integers(0, blk_n[d + 1] - blk_n[d]))
+        for j, what in ((0, "KVR"), (jb, "VR")):
+            t0_, t1_ = int(tok_n[d]) + 64 * j, min(int(tok_n[d]) + 64 * j + 64, int(tok_n[d + 1]))
+            xh = S.enc_x_host(S.memory_config(cfg).seed, l, n_tok, Hd, t0_, t1_)
+            tt = time.perf_counter()
+            ref = O.encode(xh, *w_h, wn_h[l], eps, theta, np.array([0, t1_ - t0_], np.int64),
+                           np.array([0, 1], np.int64))
+            cpu_dt.append((time.perf_counter() - tt, t1_ - t0_))
+            b = int(blk_n[d]) + j
+            got = {"K": u16(kbar[l, b]), "V": u16(vbar[l, b]),
+                   "R": u16(krt[l, 16 * (b // 16):16 * (b // 16) + 16]).reshape(8, 16, 16, 8)[:, :, b % 16].reshape(8, 128)}
+            for key, r in zip("KVR", ref):
+                if key not in what:
+                    continue
+                g64 = S.bf16_to_f32(got[key]).astype(np.float64)
+                r64 = S.bf16_to_f32(r[0]).astype(np.float64)
+                mag = np.abs(r64)
+                ulp = np.where(mag > 0, np.exp2(np.floor(np.log2(np.maximum(mag, 1e-300))) - 7), 0.0)
+                tol = np.maximum(ulp, np.exp2(-16) * mag.max(axis=-1, keepdims=True))
+                worst = max(worst, float((np.abs(g64 - r64) / tol).max()))
+    result = {
+        "metric": "encode front-end TFLOP/s (% of bf16 MFMA peak), 1M-token document set",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "offline encode: %d layers x %d tokens (%d lognormal documents) x hidden %d -> "
+                               "K, V, Kr (8 x 128 each), key RMS norm + document-wise RoPE, 64-token block "
+                               "means (%d blocks)" % (L, n_tok, lens.size, Hd, n_blk),
+                   "layers": L, "tokens": n_tok, "documents": int(lens.size), "hidden": Hd, "blocks": n_blk,
+                   "rope_theta": theta, "norm_eps": eps},
+        "tokens_per_s": round(L * n_tok / (wall / args.steps), 1),
+        "roofline": {"bound": "mfma", "kernel": "encode_kernel (msa_encode_blocks)", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flop_per_launch": flop, "algorithmic_bytes_per_launch": nbytes,
+                     "hbm_frac_at_this_rate": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "sampled_max_err_over_tol": round(worst, 4),
+    }
+    if not args.no_cpu_baseline:
+        dt = sum(c[0] for c in cpu_dt)
+        ntk = sum(c[1] for c in cpu_dt)
+        result["cpu_baseline"] = {"value": round(2.0 * Hd * 3 * 1024 * ntk / dt / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": "fp64 oracle on the %d sampled blocks (%d tokens, %.1f s)"
+                                            % (len(cpu_dt), ntk, dt)}
     print(json.dumps(result), flush=True)
 
 

@@ -249,21 +249,24 @@ int msa_sparse_decode(int32_t n_layers, int32_t B, int32_t Hq, const uint16_t* q
  * [P2 5.1 (router_k_proj: bias-free linear map to 8 x 128), 5.2 Step 1 (k_proj then
  * k_norm, v_proj, rotary positions), 3.3.1 (document-wise positions restarting at 0);
  * P1 整体设计 -> 架构]  For every memory token t at position p (its offset in its
- * document) with hidden row x_t:  k = x_t W_k, scaled per head by 1/sqrt(mean(k^2) +
+ * document) with hidden row x_t:  k = W_k x_t, scaled per head by 1/sqrt(mean(k^2) +
  * eps) and by w_norm, then rotated (pairs (e, e + 64) of each head by the angle
- * p * theta^(-e/64));  v = x_t W_v;  kr = x_t W_kr.  The three are mean-pooled over
- * the document's 64-token blocks as msa_pool_blocks does (fp32, one rounding to bf16)
- * without ever being stored per token.
+ * p * theta^(-e/64));  v = W_v x_t;  kr = W_kr x_t.  The three are mean-pooled over
+ * the document's 64-token blocks as msa_pool_blocks does (fp32 accumulation, one
+ * rounding to bf16) without ever being stored per token.  All pointers are device
+ * memory owned by the caller; only rows [0, n_tok) of x are read; the launch is
+ * asynchronous on `stream`.
  *
- *   x            [n_layers][n_tok][H] bf16, H a multiple of 32
- *   w_k, w_v, w_kr [n_layers][H][8 * 128] bf16 (input-major: row i maps hidden dim i)
+ *   x            [n_layers][n_tok][H] bf16, H a multiple of 64
+ *   w_k, w_v, w_kr [n_layers][8 * 128][H] bf16, output-major as a linear layer stores its
+ *                weight (row o maps the hidden vector to output o = head * 128 + dim)
  *   w_norm       [n_layers][128] bf16
  *   doc_tok_off, doc_blk_off, n_docs, n_blk: as for msa_pool_blocks
  *   kbar, vbar   [n_layers][n_blk][8][128] bf16 outputs
  *   krbar_route  [n_layers][tiles * 16][8][128] bf16 output (route-key tile layout)
  *   krbar_norm   [n_layers][tiles][8][16] fp32 output or NULL
  *
- * Errors: NULL pointers, sizes < 1, H % 32 != 0 (SHAPE); n_layers > 65535
+ * Errors: NULL pointers, sizes < 1, H % 64 != 0 (SHAPE); n_layers > 65535
  * (UNSUPPORTED). */
 int msa_encode_blocks(int32_t n_layers, int32_t H, const uint16_t* x, int64_t n_tok,
                       const uint16_t* w_k, const uint16_t* w_v, const uint16_t* w_kr,

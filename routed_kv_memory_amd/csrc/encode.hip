@@ -8,42 +8,37 @@
 // at 0 in every document (the same page, 3.3.1; yunpan.plus "MSA端到端可训练记忆模型完整
 // 开源…", 整体设计 -> 架构); the memory keeps the 64-token block means (3.3.2).
 //
-// Layout of the work: one 256-thread workgroup per (4 consecutive blocks, output
-// head) where an output head is 128 columns of K, V or Kr; wave w owns block w
-// (64 token rows, zero-padded past the block's end) and all 128 columns, as 4 x 8
-// accumulator tiles of v_mfma_f32_16x16x32_bf16.  The hidden dimension is walked in
-// 32-wide chunks: the 4 blocks' rows and the weight slice are staged in LDS (double
-// buffered, the next chunk's loads issued before the current one is used).  Hidden
-// rows are the A operand (16-byte LDS reads); the weights, stored input-major, reach
-// the B operand through LDS transposed reads (ds_read_b64_tr_b16).  The epilogue
-// stays in registers: the key's per-row mean square is a cross-lane sum over the 16
-// lanes of a DPP row, columns e and e + 64 of a head sit in the same lane so the
-// rotation needs no exchange, and the block mean is an in-lane sum over 16 rows plus
-// a row-swap sum over the four lane groups.  The 24 workgroups of a block group run on
-// one XCD, so its L2 serves their common hidden rows.
+// The projections are one GEMM per layer, C = X . W^T with X [tokens][H] and W
+// [3 x 8 x 128][H] (both K-contiguous, W as a linear layer stores it), so every MFMA
+// operand fragment of v_mfma_f32_16x16x32_bf16 -- 16 rows x 32 k, lane 16 g + j holding
+// row j, k 8 g .. 8 g + 7 -- is 16 contiguous bytes per lane in either operand.
+//
+// Work: one 512-thread workgroup per (4 consecutive blocks = 256 token rows, pair of
+// output heads = 256 columns of K, V or Kr).  The hidden dimension is walked in 64-wide
+// chunks staged in LDS in fragment order (each fragment 1 KiB, lane-major, so both the
+// staging stores and the operand reads are contiguous per wave): 32 row fragments and
+// 32 column fragments per chunk, two stages of 64 KiB.  Each wave loads 8 of the
+// chunk's fragments into registers one chunk ahead and stores them after computing the
+// current chunk, so a single barrier per chunk orders everything.  Wave (wr, wc)
+// accumulates block wr (64 rows) x head wc of the pair (128 columns): 4 x 8 accumulator
+// tiles, kept in VGPRs (the library is built with MFMA's VGPR form).  The epilogue stays in registers: a row's 128
+// columns sit in the 16 lanes of a DPP row (per-row mean square by a row reduction),
+// columns e and e + 64 of a head are in the same lane (the rotation needs no exchange),
+// and a block mean is an in-lane sum over 16 rows plus a sum over the 4 lane groups.
+// The 12 head pairs of a row group are placed on one XCD, so its L2 serves their
+// common hidden rows.  Rows past a block's end (or the last token) are loaded from a
+// clamped, in-bounds row and never enter a mean.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
 namespace msa {
 namespace {
 
-constexpr int kEncBlocks = 4;                  // blocks (= waves) per workgroup
-constexpr int kEncRows = kEncBlocks * kBlockTokens;
-constexpr int kKC = 32;                        // hidden columns per chunk (one MFMA k step)
-constexpr int kAStride = kKC + 8;              // bf16 per staged hidden row
-constexpr int kBStride = kDim + 8;             // bf16 per staged weight row (128 output columns)
-constexpr int kHeadOutputs = 3 * kHeads;       // K, V and Kr heads
+constexpr int kEncBlocks = 4;                  // blocks per workgroup (= 256 token rows)
+constexpr int kPairs = 3 * kHeads / 2;         // head pairs: K 0-3, V 4-7, Kr 8-11
+constexpr int kKC = 64;                        // hidden columns per staged chunk
+constexpr int kFrags = 64;                     // fragments per chunk: 2 k halves x (16 row + 16 column)
 constexpr double kInv2Pi = 0.15915494309189533577;
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the
-// 8-byte chunks addressed by lanes 4 e + i / 4 (e = 0..3).
-__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
-  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
-  return __builtin_bit_cast(uint2, r);
-}
 
 __device__ __forceinline__ int32_t find_doc(const int64_t* __restrict__ off, int32_t n, int64_t x) {
   int32_t lo = 0, hi = n;
@@ -54,26 +49,28 @@ __device__ __forceinline__ int32_t find_doc(const int64_t* __restrict__ off, int
   return lo;
 }
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 encode_kernel(int32_t H, const uint16_t* __restrict__ x, int64_t n_tok, const uint16_t* __restrict__ w_k,
               const uint16_t* __restrict__ w_v, const uint16_t* __restrict__ w_kr,
               const uint16_t* __restrict__ w_norm, float eps, double log2_theta,
               const int64_t* __restrict__ tok_off, const int64_t* __restrict__ blk_off, int32_t n_docs,
               int64_t n_blk, int64_t tiles, int64_t n_groups, uint16_t* __restrict__ kbar,
               uint16_t* __restrict__ vbar, uint16_t* __restrict__ krt, float* __restrict__ krn) {
-  __shared__ uint16_t a_s[2][kEncRows * kAStride];
-  __shared__ uint16_t b_s[2][kKC * kBStride];
+  // stage[buf][f][lane]: fragment f of the chunk (f = 16 h + mt for rows, 32 + 16 h + nt for
+  // columns, h the 32-wide half of the chunk), lane-major
+  __shared__ u32x4 stage[2][kFrags * 64];
   __shared__ int64_t s_t0[kEncBlocks], s_pos[kEncBlocks];
   __shared__ int32_t s_n[kEncBlocks];
 
-  // XCD-aware placement: the 24 output heads of a block group share the XCD of the group
+  // XCD-aware placement: the 12 head pairs of a row group share the XCD of the group
   const int64_t i = blockIdx.x;
   const int xcd = (int)(i & 7);
   const int64_t slot = i >> 3;
-  const int64_t grp = (slot / kHeadOutputs) * 8 + xcd;
-  const int ho = (int)(slot % kHeadOutputs);
+  const int64_t grp = (slot / kPairs) * 8 + xcd;
+  const int pair = (int)(slot % kPairs);
   if (grp >= n_groups) return;                 // uniform
-  const int out = ho / kHeads, head = ho % kHeads;
+  const int out = pair / 4;                    // 0 K, 1 V, 2 Kr
+  const int head0 = 2 * (pair % 4);
   const int64_t layer = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, j = lane & 15;
@@ -91,6 +88,7 @@ encode_kernel(int32_t H, const uint16_t* __restrict__ x, int64_t n_tok, const ui
       if (t0 < 0) t0 = 0;
       if (t1 > n_tok) t1 = n_tok;
       n = t1 > t0 ? (int32_t)(t1 - t0) : 0;
+      if (t0 > n_tok - 1) t0 = n_tok - 1;
       pos = (int64_t)kBlockTokens * jb;         // position of the block's first token in its document
     }
     s_t0[tid] = t0;
@@ -99,146 +97,153 @@ encode_kernel(int32_t H, const uint16_t* __restrict__ x, int64_t n_tok, const ui
   }
   __syncthreads();
 
-  const uint16_t* xl = x + layer * n_tok * (int64_t)H;
-  const uint16_t* wsel = out == 0 ? w_k : (out == 1 ? w_v : w_kr);
-  const uint16_t* wl = wsel + layer * (int64_t)H * kRow + head * kDim;
-
-  // chunk loader: A = 256 rows x 4 x 16 B, B = 32 k-rows x 16 x 16 B
-  uint4 pa[4], pb[2];
-  auto load_chunk = [&](int kc) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int u = tid + q * 256;
-      const int r = u >> 2, c = u & 3;
-      const int w = r >> 6, rr = r & 63;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (rr < s_n[w]) v = *reinterpret_cast<const uint4*>(xl + (s_t0[w] + rr) * (int64_t)H + kc + 8 * c);
-      pa[q] = v;
-    }
+  // this wave stages row fragments mt = wave, wave + 8 (row 16 (wave & 3) + j of blocks
+  // wave >> 2 and 2 + (wave >> 2)) and column fragments nt = wave, wave + 8 (column
+  // 16 wave + j of heads head0 and head0 + 1), both k halves: 8 fragments per chunk
+  const uint16_t* xrow[2];
+  const uint16_t* wrow[2];
+  {
+    const uint16_t* xl = x + layer * n_tok * (int64_t)H;
+    const uint16_t* wsel = out == 0 ? w_k : (out == 1 ? w_v : w_kr);
+    const uint16_t* wl = wsel + layer * (int64_t)kRow * H;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int u = tid + q * 256;
-      const int kk = u >> 4, c = u & 15;
-      pb[q] = *reinterpret_cast<const uint4*>(wl + (int64_t)(kc + kk) * kRow + 8 * c);
+      int64_t t = s_t0[2 * q + (wave >> 2)] + 16 * (wave & 3) + j;
+      if (t > n_tok - 1) t = n_tok - 1;
+      xrow[q] = xl + t * (int64_t)H + 8 * g;
+      const int col = (head0 + q) * kDim + 16 * wave + j;
+      wrow[q] = wl + (int64_t)col * H + 8 * g;
     }
-  };
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int u = tid + q * 256;
-      const int r = u >> 2, c = u & 3;
-      *reinterpret_cast<uint4*>(a_s[buf] + r * kAStride + 8 * c) = pa[q];
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int u = tid + q * 256;
-      const int kk = u >> 4, c = u & 15;
-      *reinterpret_cast<uint4*>(b_s[buf] + kk * kBStride + 8 * c) = pb[q];
-    }
-  };
-
-  f32x4 acc[4][8];   // rows 16 mt + 4 g + r of block `wave`, columns 16 nt + j of the head
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  load_chunk(0);
-  store_chunk(0);
-  int buf = 0;
-  // B operand source: lane j of lane group g points at columns 16 nt + 4 (j & 3) .. +3 of
-  // k-row 8 g + (j >> 2) (first four k) and of k-row 8 g + 4 + (j >> 2) (last four k)
-  const int bsrc = (8 * g + (j >> 2)) * kBStride + 4 * (j & 3);
-  for (int kc = 0; kc < H; kc += kKC, buf ^= 1) {
-    __syncthreads();   // chunk kc is in buf; every reader of buf ^ 1 is done
-    if (kc + kKC < H) load_chunk(kc + kKC);
-    bf16x8 af[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      af[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                              a_s[buf] + (wave * kBlockTokens + 16 * mt + j) * kAStride + 8 * g));
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const uint2 b0 = lds_read_tr16(b_s[buf] + bsrc + 16 * nt);
-      const uint2 b1 = lds_read_tr16(b_s[buf] + bsrc + 4 * kBStride + 16 * nt);
-      const bf16x8 bf = __builtin_bit_cast(bf16x8, (u32x4{b0.x, b0.y, b1.x, b1.y}));
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bf, acc[mt][nt], 0, 0, 0);
-    }
-    if (kc + kKC < H) store_chunk(buf ^ 1);
   }
 
-  const int64_t blk = grp * kEncBlocks + wave;
-  const int32_t n = s_n[wave];
+  uint4 pf[8];
+  auto issue = [&](int kc) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        pf[2 * q + h] = *reinterpret_cast<const uint4*>(xrow[q] + kc + 32 * h);
+        pf[4 + 2 * q + h] = *reinterpret_cast<const uint4*>(wrow[q] + kc + 32 * h);
+      }
+  };
+  auto commit = [&](int b) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        stage[b][(16 * h + wave + 8 * q) * 64 + lane] = __builtin_bit_cast(u32x4, pf[2 * q + h]);
+        stage[b][(32 + 16 * h + wave + 8 * q) * 64 + lane] = __builtin_bit_cast(u32x4, pf[4 + 2 * q + h]);
+      }
+  };
+
+  const int wr = wave & 3, wc = wave >> 2;
+  f32x4 acc[4][8];   // rows 16 m + 4 g + r of block wr, columns 16 n + j of head head0 + wc
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int b) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 af[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) af[m] = __builtin_bit_cast(bf16x8, stage[b][(16 * h + 4 * wr + m) * 64 + lane]);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const bf16x8 bf = __builtin_bit_cast(bf16x8, stage[b][(32 + 16 * h + 8 * wc + n) * 64 + lane]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bf, acc[m][n], 0, 0, 0);
+      }
+    }
+  };
+  issue(0);
+  commit(0);
+  int buf = 0;
+  // branch-free steady state (the last chunk is peeled): barrier, loads of the next chunk
+  // into registers, the current chunk's products, the next chunk's stores
+  for (int kc = kKC; kc < H; kc += kKC, buf ^= 1) {
+    __syncthreads();   // the chunk before kc is in stage buf; every reader of stage buf ^ 1 is done
+    issue(kc);
+    compute(buf);
+    commit(buf ^ 1);
+  }
+  __syncthreads();
+  compute(buf);
+
+  // epilogue, row by row: the key's per-row RMS normalisation (the 16 lanes of a DPP row
+  // hold the row's 128 columns, 8 per lane), norm weight and rotation of pairs (c, c + 64),
+  // then the block sum over valid rows, in-lane over the lane's 16 rows and over the 4 lane
+  // groups; the rotation angle p * theta^(-e/64) is formed and reduced to a fraction of a
+  // turn in fp64 (the positions of long documents would otherwise lose it to fp32 rounding)
+  const int head = head0 + wc;
+  const int64_t blk = grp * kEncBlocks + wr;
+  const int32_t nv = s_n[wr];
+  float wn[8];
+  double fturn[4];
   if (out == 0) {
-    // key: per-row RMS normalisation (the 16 lanes of a DPP row hold the row's 128
-    // columns, 8 per lane), norm weight, then the rotation of pairs (c, c + 64)
-    float wn[8];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) wn[nt] = bf16_lo(w_norm[layer * kDim + 16 * nt + j]);
-    // angle p * theta^(-e/64) formed and reduced to a fraction of a turn in fp64 (the
-    // positions of long documents would otherwise lose the angle to fp32 rounding)
-    double fturn[4];
+    for (int n = 0; n < 8; ++n) wn[n] = bf16_lo(w_norm[layer * kDim + 16 * n + j]);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) fturn[nt] = exp2(-(double)(16 * nt + j) * (1.0 / 64.0) * log2_theta) * kInv2Pi;
-    const double pos0 = (double)s_pos[wave];
+    for (int n = 0; n < 4; ++n) fturn[n] = exp2(-(double)(16 * n + j) * (1.0 / 64.0) * log2_theta) * kInv2Pi;
+  }
+  float sum[8];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+  for (int n = 0; n < 8; ++n) sum[n] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * m + 4 * g + r;        // within the block
+      float v[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) v[n] = acc[m][n][r];
+      if (out == 0) {
         float ss = 0.f;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) ss += acc[mt][nt][r] * acc[mt][nt][r];
+        for (int n = 0; n < 8; ++n) ss += v[n] * v[n];
         ss = row16_sum(ss);
         const float inv = 1.0f / sqrtf(ss * (1.0f / kDim) + eps);
-        const double p = pos0 + (double)(16 * mt + 4 * g + r);
+        const double p = (double)s_pos[wr] + (double)row;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {       // pair (16 nt + j, 16 nt + j + 64)
-          const double turns = p * fturn[nt];
+        for (int n = 0; n < 4; ++n) {        // pair (16 n + j, 16 n + j + 64)
+          const double turns = p * fturn[n];
           const float half_turns = (float)(2.0 * (turns - rint(turns)));   // angle / pi in [-1, 1]
           float sn, cs;
           sincospif(half_turns, &sn, &cs);
-          const float a = acc[mt][nt][r] * inv * wn[nt], c = acc[mt][nt + 4][r] * inv * wn[nt + 4];
-          acc[mt][nt][r] = a * cs - c * sn;
-          acc[mt][nt + 4][r] = c * cs + a * sn;
+          const float a = v[n] * inv * wn[n], c = v[n + 4] * inv * wn[n + 4];
+          v[n] = a * cs - c * sn;
+          v[n + 4] = c * cs + a * sn;
         }
       }
-  }
-  // block mean: in-lane over the lane's 16 rows (valid ones), then over the 4 lane groups
-  float mean[8];
-  const float inv_n = n > 0 ? 1.0f / (float)n : 0.f;
+      const bool valid = row < nv;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    float sum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * mt + 4 * g + r < n) sum += acc[mt][nt][r];
-    mean[nt] = rows4_sum(sum) * inv_n;
-  }
-  // every lane now holds the 8 column means of its j; lane group g writes nt = 2 g, 2 g + 1
-  if (blk < n_blk) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int nt = 2 * g + q;
-      const int col = 16 * nt + j;
-      const uint16_t bits = (uint16_t)f32_to_bf16_rne(mean[nt]);
-      if (out == 0) kbar[((layer * n_blk + blk) * kHeads + head) * kDim + col] = bits;
-      else if (out == 1) vbar[((layer * n_blk + blk) * kHeads + head) * kDim + col] = bits;
+      for (int n = 0; n < 8; ++n) sum[n] += valid ? v[n] : 0.f;
     }
-  }
-  if (out == 2) {
+  const float inv_n = nv > 0 ? 1.0f / (float)nv : 0.f;
+  float mean[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) mean[n] = rows4_sum(sum[n]) * inv_n;
+  // lane group g writes the columns of n = 2 g, 2 g + 1
+  if (out < 2) {
+    if (blk < n_blk) {
+      uint16_t* dst = (out == 0 ? kbar : vbar) + ((layer * n_blk + blk) * kHeads + head) * kDim;
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const int n = 2 * g + e2;
+        dst[16 * n + j] = (uint16_t)f32_to_bf16_rne(mean[n]);
+      }
+    }
+  } else {
     // route layout: [layer][tile][h][c][b][8]; padding blocks of the last tile get zeros
     const int64_t tile = blk / kTile;
     const int b = (int)(blk % kTile);
     float ssr = 0.f;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int nt = 2 * g + q;
-      const int col = 16 * nt + j;
-      const uint32_t bits = blk < n_blk ? f32_to_bf16_rne(mean[nt]) : 0u;
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int n = 2 * g + e2;
+      const int col = 16 * n + j;
+      const uint32_t bits = blk < n_blk ? f32_to_bf16_rne(mean[n]) : 0u;
       if (tile < tiles)
         krt[(((layer * tiles + tile) * kHeads + head) * (kTile * 16) + (col >> 3) * kTile + b) * 8 + (col & 7)] =
             (uint16_t)bits;
@@ -264,9 +269,10 @@ hipError_t launch_encode(int32_t L, int32_t H, const uint16_t* x, int64_t n_tok,
   // every block of every tile (padding blocks included, so the route layout is complete)
   const int64_t n_groups = tiles * kTile / kEncBlocks;
   const int64_t groups8 = (n_groups + 7) / 8 * 8;
-  const dim3 grid((unsigned)(groups8 * kHeadOutputs), (unsigned)L);
-  hipLaunchKernelGGL(encode_kernel, grid, dim3(256), 0, s, H, x, n_tok, w_k, w_v, w_kr, w_norm, eps,
-                     log2((double)theta), doc_tok_off, doc_blk_off, n_docs, n_blk, tiles, n_groups, kbar, vbar, krt, krn);
+  const dim3 grid((unsigned)(groups8 * kPairs), (unsigned)L);
+  hipLaunchKernelGGL(encode_kernel, grid, dim3(512), 0, s, H, x, n_tok, w_k, w_v, w_kr, w_norm, eps,
+                     log2((double)theta), doc_tok_off, doc_blk_off, n_docs, n_blk, tiles, n_groups, kbar, vbar,
+                     krt, krn);
   return hipGetLastError();
 }
 

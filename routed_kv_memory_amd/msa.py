@@ -246,7 +246,7 @@ def msa_sparse_prefill(q, ctx_k, ctx_v, ctx_len, loc_k, loc_v, loc_len, scale, o
 
 def msa_encode_blocks(x, w_k, w_v, w_kr, w_norm, eps, theta, doc_tok_off, doc_blk_off, n_blk, kbar, vbar,
                       krbar_route, krbar_norm=None, stream=None):
-    """x [L][n_tok][H]; W_* [L][H][1024]; w_norm [L][128]; outputs as msa_pool_blocks."""
+    """x [L][n_tok][H]; W_* [L][1024][H] (output-major); w_norm [L][128]; outputs as msa_pool_blocks."""
     L, n_tok, H = x.shape
     n_docs = doc_tok_off.numel() - 1
     _check("msa_encode_blocks", lib().msa_encode_blocks(

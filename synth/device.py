@@ -150,3 +150,24 @@ class DeviceInputs:
         ll = torch.full((L, B), T, dtype=torch.int32, device=self.device)
         return q, ck, cv, ctx_len, lk, lv, ll
 
+    # ------------------------------------------------------------- encode front-end
+    def encode_inputs(self, hidden: int = S.ENC_HIDDEN, n_layers: int = None):
+        """Inputs of the encode front-end over this config's documents: (doc_tok_off int64 CPU,
+        x [L][n_tok][hidden], W_k, W_v, W_kr [L][1024][hidden] (output-major, as a linear layer
+        stores them), w_norm [L][128]), all bf16."""
+        mem = self.mem
+        L = mem.n_layers if n_layers is None else n_layers
+        tok = S.doc_tok_offsets(mem)
+        n_tok = int(tok[-1])
+        seed = mem.seed
+        x = torch.empty((L, n_tok, hidden), dtype=torch.bfloat16, device=self.device)
+        self.gen.fill(x, seed, S.S_ENC_X)
+        ws = []
+        for stream in (S.S_ENC_WK, S.S_ENC_WV, S.S_ENC_WKR):
+            w = torch.empty((L, S.ROW, hidden), dtype=torch.bfloat16, device=self.device)
+            self.gen.fill(w, seed, stream)
+            w.mul_(S.enc_weight_scale(hidden))          # a power of two: exact in bf16
+            ws.append(w)
+        wn = torch.from_numpy(S.enc_norm_weight_host(seed, L).view(np.int16)).to(self.device).view(torch.bfloat16)
+        return torch.as_tensor(tok), x, ws[0], ws[1], ws[2], wn
+

@@ -48,6 +48,8 @@ S_QR, S_NEEDLE = 7, 8
 S_DEC_Q, S_LOC_K, S_LOC_V = 9, 10, 11
 S_TABLES = 12
 S_PF_Q, S_PF_CTX_K, S_PF_CTX_V, S_PF_DOCS = 13, 14, 15, 16   # multi-token prefill inputs
+S_ENC_X, S_ENC_WK, S_ENC_WV, S_ENC_WKR, S_ENC_WN = 17, 18, 19, 20, 21   # encode front-end inputs
+ENC_HIDDEN = 2560          # hidden size of the encode workload (the pages' 4B backbone)
 
 SEED0 = 0x4D534100
 
@@ -348,3 +350,30 @@ class DeviceGen:
         if rc:
             raise RuntimeError("synth_plant failed: hip error %d" % rc)
         return rows_t
+
+
+# --------------------------------------------------------------------------- encode inputs
+
+def enc_weight_scale(hidden: int) -> float:
+    """Power of two nearest 1/sqrt(hidden): scaling N(0,1) bf16 weights by it is exact and
+    gives projections of about unit variance."""
+    return float(2.0 ** -round(math.log2(math.sqrt(hidden))))
+
+
+def enc_weights_host(seed: int, stream: int, layer: int, hidden: int) -> np.ndarray:
+    """Layer `layer` of a [L][1024][hidden] projection weight, stored as a linear layer
+    stores it (output-major), as uint16 bf16 [1024][hidden]."""
+    raw = fill_host(ROW * hidden, seed, stream, layer * ROW * hidden).reshape(ROW, hidden)
+    return f32_to_bf16(bf16_to_f32(raw) * np.float32(enc_weight_scale(hidden)))
+
+
+def enc_norm_weight_host(seed: int, n_layers: int) -> np.ndarray:
+    """[L][128] key-norm weights near 1 (uint16 bf16)."""
+    z = bf16_to_f32(fill_host(n_layers * D, seed, S_ENC_WN))
+    return f32_to_bf16(np.float32(1.0) + np.float32(0.25) * z).reshape(n_layers, D)
+
+
+def enc_x_host(seed: int, layer: int, n_tok: int, hidden: int, t0: int, t1: int) -> np.ndarray:
+    """Hidden rows [t0, t1) of layer `layer` of x [L][n_tok][hidden] (uint16 bf16)."""
+    return fill_host((t1 - t0) * hidden, seed, S_ENC_X, (layer * n_tok + t0) * hidden).reshape(t1 - t0, hidden)
+

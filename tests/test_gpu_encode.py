@@ -60,7 +60,8 @@ def run_encode(x, w, wn, eps, theta, tok, with_norms=True):
     krt, krn = alloc_route_keys(L, n_blk)
     krt.view(torch.int16).fill_(-1)
     krn.fill_(-1.0)
-    msa.msa_encode_blocks(to_dev_bf16(x), *[to_dev_bf16(a) for a in w], to_dev_bf16(wn), eps, theta,
+    # the library takes the weights output-major ([L][1024][H]), the oracle input-major
+    msa.msa_encode_blocks(to_dev_bf16(x), *[to_dev_bf16(a.transpose(0, 2, 1)) for a in w], to_dev_bf16(wn), eps, theta,
                           torch.from_numpy(tok).to(DEV), blk.to(DEV), n_blk, kbar, vbar, krt,
                           krn if with_norms else None)
     torch.cuda.synchronize()
@@ -88,11 +89,11 @@ def check_layerwise(x, w, wn, eps, theta, tok, with_norms=True):
 
 def test_ragged_documents_all_outputs():
     """Documents of 1, 63, 64, 65 tokens, an empty one, and longer ones; two layers."""
-    print("case: encode ragged H=96", flush=True)
+    print("case: encode ragged H=192", flush=True)
     rng = np.random.default_rng(301)
     lens = np.array([1, 63, 64, 65, 0, 130, 200, 7, 640, 129])
     tok = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
-    L, Hd = 2, 96
+    L, Hd = 2, 192
     x = S.f32_to_bf16(rng.standard_normal((L, int(tok[-1]), Hd)).astype(np.float32))
     w, wn = make_weights(rng, L, Hd)
     check_layerwise(x, w, wn, 1e-6, 1e6, tok)
@@ -115,7 +116,7 @@ def test_long_document_positions(theta):
     print("case: encode long document theta=%g" % theta, flush=True)
     rng = np.random.default_rng(303)
     tok = np.array([0, 5, 12005], np.int64)
-    L, Hd = 1, 32
+    L, Hd = 1, 64
     x = S.f32_to_bf16(rng.standard_normal((L, 12005, Hd)).astype(np.float32))
     w, wn = make_weights(rng, L, Hd)
     check_layerwise(x, w, wn, 1e-6, theta, tok)
