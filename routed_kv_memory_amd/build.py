@@ -15,6 +15,9 @@ ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden", "--offload-arch=" + ARCH,
          # packed fp32 VALU forms are kept out of generated code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in VGPRs: the AGPR form makes the register allocator copy
+         # accumulators between the two files on every loop iteration
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

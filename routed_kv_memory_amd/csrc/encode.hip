@@ -165,6 +165,7 @@ encode_kernel(int32_t H, const uint16_t* __restrict__ x, int64_t n_tok, const ui
   for (int kc = kKC; kc < H; kc += kKC, buf ^= 1) {
     __syncthreads();   // the chunk before kc is in stage buf; every reader of stage buf ^ 1 is done
     issue(kc);
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the products (no sinking)
     compute(buf);
     commit(buf ^ 1);
   }

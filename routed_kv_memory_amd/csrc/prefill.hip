@@ -53,8 +53,12 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
-template <int G>
-__global__ void __launch_bounds__(64 * G)
+// G query heads per KV head; HPW of them per wave; TB 16-token query blocks per workgroup.
+// Waves: (G / HPW) x TB; wave w takes token block w / (G / HPW) and heads
+// HPW * (w % (G / HPW)) .. +HPW-1 of the group.  The heads of a wave share every K
+// fragment and every V^T fragment read from LDS, and the tokens' mask.
+template <int G, int HPW, int TB>
+__global__ void __launch_bounds__(64 * (G / HPW) * TB)
 prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint16_t* __restrict__ ctx_k,
                const uint16_t* __restrict__ ctx_v, const int32_t* __restrict__ ctx_len, int32_t max_ctx,
                const uint16_t* __restrict__ loc_k, const uint16_t* __restrict__ loc_v,
@@ -62,14 +66,16 @@ prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint
   __shared__ uint16_t k_s[2][kKeyTile * kKStride];   // double buffered: one barrier per tile
   __shared__ uint16_t v_s[2][kKeyTile * kVStride];
 
-  constexpr int NT = 64 * G;
-  const int t0 = blockIdx.x * kQBlock;
-  const int kvh = blockIdx.y;
-  const int64_t lb = blockIdx.z;
+  constexpr int WPB = G / HPW;             // waves per token block
+  constexpr int NT = 64 * WPB * TB;
   const int tid = threadIdx.x;
-  const int hh = tid >> 6;                 // query head within the group (= wave)
+  const int wave = tid >> 6;
   const int lane = tid & 63;
   const int g = lane >> 4, j = lane & 15;  // lane group, query token t0 + j
+  const int t0 = (blockIdx.x * TB + wave / WPB) * kQBlock;
+  const int hq0 = blockIdx.y * G + HPW * (wave % WPB);
+  const int kvh = blockIdx.y;
+  const int64_t lb = blockIdx.z;
   const float ninf = -__builtin_huge_valf();
 
   int32_t clen = ctx_len[lb];
@@ -81,54 +87,55 @@ prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint
     int v = llen - T + t + 1;
     return v < 0 ? 0 : (v > llen ? llen : v);
   };
-  const int t_last = t0 + kQBlock - 1 < T - 1 ? t0 + kQBlock - 1 : T - 1;
-  const int32_t n_keys = clen + visible(t_last);
+  // keys of the workgroup (its last token's limit) and of this wave's block
+  const int tw_last = (int)blockIdx.x * TB * kQBlock + TB * kQBlock - 1;
+  const int32_t n_keys = clen + visible(tw_last < T - 1 ? tw_last : T - 1);
+  const int tb_last = t0 + kQBlock - 1 < T - 1 ? t0 + kQBlock - 1 : T - 1;
+  const int32_t n_keys_w = t0 < T ? clen + visible(tb_last) : 0;
   const int tok = t0 + j;
   const int vis_tok = tok < T ? visible(tok) : 0;
 
-  // query block as B fragments: token t0 + j, dims 32 s + 8 g .. +7
-  const int hq = kvh * G + hh;
-  bf16x8 qf[4];
+  // query blocks as B fragments: token t0 + j, dims 32 s + 8 g .. +7, per head
+  bf16x8 qf[HPW][4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (tok < T) v = *reinterpret_cast<const u32x4*>(q + (((lb * T + tok) * Hq + hq) * kDim) + 32 * s + 8 * g);
-    qf[s] = __builtin_bit_cast(bf16x8, v);
-  }
+  for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (tok < T)
+        v = *reinterpret_cast<const u32x4*>(q + (((lb * T + tok) * Hq + hq0 + hh) * kDim) + 32 * s + 8 * g);
+      qf[hh][s] = __builtin_bit_cast(bf16x8, v);
+    }
 
   const uint16_t* ck = ctx_k + (lb * max_ctx) * (int64_t)kRow + kvh * kDim;
   const uint16_t* cv = ctx_v + (lb * max_ctx) * (int64_t)kRow + kvh * kDim;
   const uint16_t* lk = loc_k + (lb * (int64_t)max_loc) * kRow + kvh * kDim;
   const uint16_t* lv = loc_v + (lb * (int64_t)max_loc) * kRow + kvh * kDim;
 
-  // tile loader: 32 keys x 16 chunks of 16 B for K and for V
+  // tile loader: 32 keys x 16 chunks of 16 B for K and for V.  Rows past the last key
+  // are loaded from the last key (in bounds, finite) and masked out of the scores, so the
+  // loads carry no branch and no zero fill.
   constexpr int kPer = (kKeyTile * 16 + NT - 1) / NT;
-  uint4 pk[kPer], pv[kPer];
+  static_assert(kPer * NT == kKeyTile * 16, "the tile's chunks split evenly over the threads");
+  u32x4 pk[kPer], pv[kPer];
   auto load_tile = [&](int32_t k0) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int u = tid + i * NT;
       const int kk = u >> 4, c = u & 15;
-      uint4 kw = make_uint4(0, 0, 0, 0), vw = kw;
-      const int32_t row = k0 + kk;
-      if (u < kKeyTile * 16 && row < n_keys) {
-        const uint16_t* ks = row < clen ? ck + (int64_t)row * kRow : lk + (int64_t)(row - clen) * kRow;
-        const uint16_t* vs = row < clen ? cv + (int64_t)row * kRow : lv + (int64_t)(row - clen) * kRow;
-        kw = *reinterpret_cast<const uint4*>(ks + c * 8);
-        vw = *reinterpret_cast<const uint4*>(vs + c * 8);
-      }
-      pk[i] = kw;
-      pv[i] = vw;
+      const int32_t row = k0 + kk < n_keys ? k0 + kk : n_keys - 1;
+      const int64_t off = (row < clen ? (int64_t)row : (int64_t)(row - clen)) * kRow + c * 8;
+      pk[i] = *reinterpret_cast<const u32x4*>((row < clen ? ck : lk) + off);
+      pv[i] = *reinterpret_cast<const u32x4*>((row < clen ? cv : lv) + off);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int u = tid + i * NT;
-      if (u >= kKeyTile * 16) break;
       const int kk = u >> 4, c = u & 15;
-      *reinterpret_cast<uint4*>(k_s[buf] + kk * kKStride + c * 8) = pk[i];
-      *reinterpret_cast<uint4*>(v_s[buf] + kk * kVStride + c * 8) = pv[i];
+      *reinterpret_cast<u32x4*>(k_s[buf] + kk * kKStride + c * 8) = pk[i];
+      *reinterpret_cast<u32x4*>(v_s[buf] + kk * kVStride + c * 8) = pv[i];
     }
   };
 
@@ -137,114 +144,139 @@ prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint
   // probabilities stay below 2^kSlack and the accumulators are rescaled rarely.
   constexpr float kSlack = 8.f;
   const float scale2 = scale * 1.4426950408889634f;
-  float m_run = ninf, l_lane = 0.f;
-  f32x4 o[8];   // O^T: dims 16 dt + 4 g + r, token t0 + j
+  float m_run[HPW], l_lane[HPW];
+  f32x4 o[HPW][8];   // O^T: dims 16 dt + 4 g + r, token t0 + j
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int hh = 0; hh < HPW; ++hh) {
+    m_run[hh] = ninf;
+    l_lane[hh] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[hh][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  // keys every token of the block may see: the first token's limit
+  // keys every token of the wave's block may see: its first token's limit
   const int32_t all_visible = clen + (t0 < T ? visible(t0) : 0);
   if (n_keys > 0) {
     load_tile(0);
     store_tile(0);
   }
+  // every load issued so far (the query fragments, the first tile) completes here, so the
+  // loop's wait bookkeeping starts clean and waits only for each tile's own loads
+  __builtin_amdgcn_s_waitcnt(0);
   int buf = 0;
   for (int32_t k0 = 0; k0 < n_keys; k0 += kKeyTile, buf ^= 1) {
     __syncthreads();   // tile k0 is in buf; every reader of buf ^ 1 (the tile before) is done
     if (k0 + kKeyTile < n_keys) load_tile(k0 + kKeyTile);
-    const uint16_t* kt = k_s[buf];
-
-    // S^T for keys k0 + 16 h2 + 4 g + r (h2 = 0, 1), token t0 + j
-    f32x4 sc[2];
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the tile's products
+    if (k0 < n_keys_w) {                       // uniform per wave: the block sees part of the tile
+      const uint16_t* kt = k_s[buf];
+      // S^T for keys k0 + 16 h2 + 4 g + r (h2 = 0, 1), token t0 + j, per head
+      f32x4 sc[HPW][2];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4 kw = *reinterpret_cast<const u32x4*>(kt + (16 * h2 + j) * kKStride + 32 * s + 8 * g);
-        sc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[s], sc[h2], 0, 0, 0);
-      }
-    }
-    // scale to log2 units and mask (tiles every token of the block sees whole need no mask)
-    float mt = ninf;
-    if (k0 + kKeyTile <= all_visible) {
+        for (int hh = 0; hh < HPW; ++hh) sc[hh][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 kw = *reinterpret_cast<const u32x4*>(kt + (16 * h2 + j) * kKStride + 32 * s + 8 * g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sc[h2][r] *= scale2;
-          mt = fmaxf(mt, sc[h2][r]);
+          for (int hh = 0; hh < HPW; ++hh)
+            sc[hh][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[hh][s],
+                                                                 sc[hh][h2], 0, 0, 0);
         }
-    } else {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int32_t key = k0 + 16 * h2 + 4 * g + r;
-          const bool ok = key < n_keys && (key < clen || key - clen < vis_tok);
-          const float v = ok ? sc[h2][r] * scale2 : ninf;
-          sc[h2][r] = v;
-          mt = fmaxf(mt, v);
-        }
-    }
-    mt = rows4_max(mt);                      // over the tile's 32 keys of token t0 + j
-    // raise the reference maximum only past the slack (ballot: most tiles skip the rescale)
-    const bool raise = mt > m_run + kSlack;
-    float alpha = 1.f;
-    if (__ballot(raise)) {
-      const float m_new = raise ? mt : m_run;
-      alpha = m_run == ninf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_lane *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-    }
-    const float m_use = m_run == ninf ? 0.f : m_run;   // a token with no visible key yet
-    float psum = 0.f;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sc[h2][r] - m_use);
-        sc[h2][r] = p;
-        psum += p;
       }
-    l_lane += psum;
-    // P^T as the B operand: k slot 8 g + e holds key 4 g + e (e < 4) or 16 + 4 g + e - 4.
-    // P = P_hi + P_lo with both parts in bf16 (two products), so the probabilities
-    // enter the matrix cores with ~16 significant bits rather than 8.
-    u32x4 pwh, pwl;
+      const bool whole = k0 + kKeyTile <= all_visible;   // no mask needed
+      bf16x8 pfh[HPW], pfl[HPW];
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const float p0 = sc[e2 >> 1][2 * (e2 & 1)], p1 = sc[e2 >> 1][2 * (e2 & 1) + 1];
-      const uint32_t hw = pack2_bf16(p0, p1);
-      pwh[e2] = hw;
-      pwl[e2] = pack2_bf16(p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u));
-    }
-    const bf16x8 pfh = __builtin_bit_cast(bf16x8, pwh), pfl = __builtin_bit_cast(bf16x8, pwl);
-    // V^T fragments by transposed reads of the row-major V tile: lane (g, j) of the
-    // A operand needs dim 16 dt + j of keys 4 g + e and 16 + 4 g + e (e = 0..3), so
-    // source lane j points at dims 16 dt + 4 (j & 3) .. +3 of key 4 g + (j >> 2).
-    const uint16_t* vsrc = v_s[buf] + (4 * g + (j >> 2)) * kVStride + 4 * (j & 3);
+      for (int hh = 0; hh < HPW; ++hh) {
+        // scale to log2 units and mask (tiles every token of the block sees whole need no mask)
+        float mt = ninf;
+        if (whole) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint2 a0 = lds_read_tr16(vsrc + 16 * dt);
-      const uint2 a1 = lds_read_tr16(vsrc + 16 * kVStride + 16 * dt);
-      const u32x4 vw = {a0.x, a0.y, a1.x, a1.y};
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vw), pfh, o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vw), pfl, o[dt], 0, 0, 0);
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              sc[hh][h2][r] *= scale2;
+              mt = fmaxf(mt, sc[hh][h2][r]);
+            }
+        } else {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int32_t key = k0 + 16 * h2 + 4 * g + r;
+              const bool ok = key < n_keys && (key < clen || key - clen < vis_tok);
+              const float v = ok ? sc[hh][h2][r] * scale2 : ninf;
+              sc[hh][h2][r] = v;
+              mt = fmaxf(mt, v);
+            }
+        }
+        mt = rows4_max(mt);                    // over the tile's 32 keys of token t0 + j
+        // raise the reference maximum only past the slack (ballot: most tiles skip the rescale)
+        const bool raise = mt > m_run[hh] + kSlack;
+        if (__ballot(raise)) {
+          const float m_new = raise ? mt : m_run[hh];
+          const float alpha = m_run[hh] == ninf ? 0.f : __builtin_amdgcn_exp2f(m_run[hh] - m_new);
+          m_run[hh] = m_new;
+          l_lane[hh] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[hh][dt] *= alpha;
+        }
+        const float m_use = m_run[hh] == ninf ? 0.f : m_run[hh];   // a token with no visible key yet
+        float psum = 0.f;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(sc[hh][h2][r] - m_use);
+            sc[hh][h2][r] = p;
+            psum += p;
+          }
+        l_lane[hh] += psum;
+        // P^T as the B operand: k slot 8 g + e holds key 4 g + e (e < 4) or 16 + 4 g + e - 4.
+        // P = P_hi + P_lo with both parts in bf16 (two products), so the probabilities
+        // enter the matrix cores with ~16 significant bits rather than 8.
+        u32x4 pwh, pwl;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float p0 = sc[hh][e2 >> 1][2 * (e2 & 1)], p1 = sc[hh][e2 >> 1][2 * (e2 & 1) + 1];
+          const uint32_t hw = pack2_bf16(p0, p1);
+          pwh[e2] = hw;
+          pwl[e2] = pack2_bf16(p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u));
+        }
+        pfh[hh] = __builtin_bit_cast(bf16x8, pwh);
+        pfl[hh] = __builtin_bit_cast(bf16x8, pwl);
+      }
+      // V^T fragments by transposed reads of the row-major V tile: lane (g, j) of the
+      // A operand needs dim 16 dt + j of keys 4 g + e and 16 + 4 g + e (e = 0..3), so
+      // source lane j points at dims 16 dt + 4 (j & 3) .. +3 of key 4 g + (j >> 2).
+      const uint16_t* vsrc = v_s[buf] + (4 * g + (j >> 2)) * kVStride + 4 * (j & 3);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint2 a0 = lds_read_tr16(vsrc + 16 * dt);
+        const uint2 a1 = lds_read_tr16(vsrc + 16 * kVStride + 16 * dt);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, (u32x4{a0.x, a0.y, a1.x, a1.y}));
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          o[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfh[hh], o[hh][dt], 0, 0, 0);
+          o[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl[hh], o[hh][dt], 0, 0, 0);
+        }
+      }
     }
     if (k0 + kKeyTile < n_keys) store_tile(buf ^ 1);
   }
 
-  const float l_tok = rows4_sum(l_lane);
-  if (tok < T) {
-    const float inv = l_tok > 0.f ? 1.0f / l_tok : 0.f;
-    float* dst = out + ((lb * T + tok) * Hq + hq) * kDim + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(dst + 16 * dt) =
-          make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+  for (int hh = 0; hh < HPW; ++hh) {
+    const float l_tok = rows4_sum(l_lane[hh]);
+    if (tok < T) {
+      const float inv = l_tok > 0.f ? 1.0f / l_tok : 0.f;
+      float* dst = out + ((lb * T + tok) * Hq + hq0 + hh) * kDim + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<float4*>(dst + 16 * dt) =
+            make_float4(o[hh][dt][0] * inv, o[hh][dt][1] * inv, o[hh][dt][2] * inv, o[hh][dt][3] * inv);
+    }
   }
 }
 
@@ -255,18 +287,19 @@ hipError_t launch_prefill(int32_t L, int32_t B, int32_t T, int32_t Hq, const uin
                           const uint16_t* loc_v, const int32_t* loc_len, int32_t max_loc, float scale, float* out,
                           hipStream_t s) {
   const int G = Hq / kHeads;
-  const dim3 grid((unsigned)((T + kQBlock - 1) / kQBlock), kHeads, (unsigned)(L * B));
+#define MSA_PREFILL_LAUNCH(GV, HPWV, TBV)                                                                       \
+  hipLaunchKernelGGL((prefill_kernel<GV, HPWV, TBV>),                                                          \
+                     dim3((unsigned)((T + kQBlock * (TBV) - 1) / (kQBlock * (TBV))), kHeads, (unsigned)(L * B)), \
+                     dim3(64 * ((GV) / (HPWV)) * (TBV)), 0, s, T, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx, loc_k,   \
+                     loc_v, loc_len, max_loc, scale, out)
   switch (G) {
-    case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(64), 0, s, T, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
-                               loc_k, loc_v, loc_len, max_loc, scale, out); break;
-    case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(128), 0, s, T, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
-                               loc_k, loc_v, loc_len, max_loc, scale, out); break;
-    case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(256), 0, s, T, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
-                               loc_k, loc_v, loc_len, max_loc, scale, out); break;
-    case 8: hipLaunchKernelGGL(prefill_kernel<8>, grid, dim3(512), 0, s, T, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
-                               loc_k, loc_v, loc_len, max_loc, scale, out); break;
+    case 1: MSA_PREFILL_LAUNCH(1, 1, 4); break;
+    case 2: MSA_PREFILL_LAUNCH(2, 2, 2); break;
+    case 4: MSA_PREFILL_LAUNCH(4, 2, 2); break;
+    case 8: MSA_PREFILL_LAUNCH(8, 2, 1); break;
     default: return hipErrorInvalidValue;
   }
+#undef MSA_PREFILL_LAUNCH
   return hipGetLastError();
 }
 
