@@ -34,16 +34,40 @@ POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 # WRITE_SIZE rocprofv3 passes (scaled by a 1 GiB calibration kernel) recorded in
 # profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
 # sources' digest differs, the figure is stale and bench.py reports null.
-SCAN_TRAFFIC_BYTES = 57.692e9
-SCAN_TRAFFIC_SOURCE_DIGEST = "6dad12db310dcb54ad0048b548eb18836a8ddbf8d02ed88edf590d65177fe1df"
+SCAN_TRAFFIC_BYTES = 57.694e9
+SCAN_TRAFFIC_SOURCE_DIGEST = "c5efc6a8e7e028e0cb0ad7ace550b61865b4074a042a374efa7a5a846274a6fd"
+
+
+# HBM traffic of one encode launch (18 layers, 1M-token document set), FETCH_SIZE + WRITE_SIZE
+# passes scaled by the 1 GiB calibration copy, recorded in profiles/encode_1m_tokens.md; valid for
+# the kernel source it was measured on only.
+ENCODE_TRAFFIC_BYTES = 1259.8e9
+ENCODE_TRAFFIC_SOURCE_DIGEST = "0885938f6f19547c7d79c5bf2f57bca659daa8431d591b0767d1b943db2c9705"
+
+
+def source_digest(files=("route.hip", "msa_device.hpp")):
+    import hashlib
+    csrc = os.path.join(ROOT, "routed_kv_memory_amd", "csrc")
+    parts = [hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest() for f in files]
+    return hashlib.sha256("".join(parts).encode()).hexdigest()
 
 
 def scan_source_digest():
-    import hashlib
-    csrc = os.path.join(ROOT, "routed_kv_memory_amd", "csrc")
-    parts = [hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
-             for f in ("route.hip", "msa_device.hpp")]
-    return hashlib.sha256("".join(parts).encode()).hexdigest()
+    return source_digest()
+
+
+def calibration_copy(dev="cuda"):
+    """Kernels of known traffic for scaling hardware byte counters: a 1 GiB fill, then a
+    1 GiB elementwise copy (reads 1 GiB, writes 1 GiB)."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(7)
+    torch.cuda.synchronize()
+    torch.add(src, 1, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    return 1 << 30
 
 
 def parse():
@@ -263,13 +287,7 @@ def main():
 
     if args.calibrate_copy:
         del ck, cv
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(7)                        # writes 1 GiB
-        torch.cuda.synchronize()
-        torch.add(src, 1, out=dst)          # reads 1 GiB, writes 1 GiB
-        torch.cuda.synchronize()
-        result["calibration_copy_bytes"] = 1 << 30
+        result["calibration_copy_bytes"] = calibration_copy(dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, n_blk, blk.numpy(), args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -620,7 +638,8 @@ def encode_bench(args):
     tok_n, blk_n = tok.numpy(), blk.numpy()
     lens = np.diff(tok_n)
     rng = np.random.default_rng(7)
-    samples = [(0, int(rng.integers(0, lens.size))), (L - 1, int(rng.integers(0, lens.size)))]
+    n_samples = 2 if args.no_cpu_baseline else 8      # the oracle calls double as the CPU-baseline sample
+    samples = [(int(l), int(rng.integers(0, lens.size))) for l in np.linspace(0, L - 1, n_samples).round()]
     u16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     wn_h = u16(wn)
     worst = 0.0
@@ -661,10 +680,15 @@ def encode_bench(args):
         "tokens_per_s": round(L * n_tok / (wall / args.steps), 1),
         "roofline": {"bound": "mfma", "kernel": "encode_kernel (msa_encode_blocks)", "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flop_per_launch": flop, "algorithmic_bytes_per_launch": nbytes,
+                     "traffic": (ENCODE_TRAFFIC_BYTES if source_digest(("encode.hip", "msa_device.hpp"))
+                                 == ENCODE_TRAFFIC_SOURCE_DIGEST else None), "traffic_unit": "bytes per launch",
+                     "algorithmic_flop_per_launch": flop, "algorithmic_bytes_per_launch": nbytes,
                      "hbm_frac_at_this_rate": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "sampled_max_err_over_tol": round(worst, 4),
     }
+    if args.calibrate_copy:
+        del x
+        result["calibration_copy_bytes"] = calibration_copy()
     if not args.no_cpu_baseline:
         dt = sum(c[0] for c in cpu_dt)
         ntk = sum(c[1] for c in cpu_dt)

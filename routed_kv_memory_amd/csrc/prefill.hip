@@ -34,25 +34,6 @@ constexpr int kKeyTile = 32;           // keys per step
 constexpr int kKStride = kDim + 8;     // bf16 per staged K row
 constexpr int kVStride = kDim + 8;     // bf16 per staged V row
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the
-// 8-byte chunks addressed by lanes 4 e + i / 4 (e = 0..3) -- a 16 x 4 transpose of
-// 16-bit elements.
-__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
-  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
-  return __builtin_bit_cast(uint2, r);
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
-}
-
 // G query heads per KV head; HPW of them per wave; TB 16-token query blocks per workgroup.
 // Waves: (G / HPW) x TB; wave w takes token block w / (G / HPW) and heads
 // HPW * (w % (G / HPW)) .. +HPW-1 of the group.  The heads of a wave share every K
