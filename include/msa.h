@@ -257,7 +257,7 @@ int msa_sparse_decode(int32_t n_layers, int32_t B, int32_t Hq, const uint16_t* q
  * memory owned by the caller; only rows [0, n_tok) of x are read; the launch is
  * asynchronous on `stream`.
  *
- *   x            [n_layers][n_tok][H] bf16, H a multiple of 64
+ *   x            [n_layers][n_tok][H] bf16, H a multiple of 128
  *   w_k, w_v, w_kr [n_layers][8 * 128][H] bf16, output-major as a linear layer stores its
  *                weight (row o maps the hidden vector to output o = head * 128 + dim)
  *   w_norm       [n_layers][128] bf16
@@ -266,7 +266,7 @@ int msa_sparse_decode(int32_t n_layers, int32_t B, int32_t Hq, const uint16_t* q
  *   krbar_route  [n_layers][tiles * 16][8][128] bf16 output (route-key tile layout)
  *   krbar_norm   [n_layers][tiles][8][16] fp32 output or NULL
  *
- * Errors: NULL pointers, sizes < 1, H % 64 != 0 (SHAPE); n_layers > 65535
+ * Errors: NULL pointers, sizes < 1, H % 128 != 0 (SHAPE); n_layers > 65535
  * (UNSUPPORTED). */
 int msa_encode_blocks(int32_t n_layers, int32_t H, const uint16_t* x, int64_t n_tok,
                       const uint16_t* w_k, const uint16_t* w_v, const uint16_t* w_kr,

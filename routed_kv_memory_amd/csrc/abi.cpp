@@ -289,7 +289,7 @@ MSA_API int msa_encode_blocks(int32_t n_layers, int32_t H, const uint16_t* x, in
                               uint16_t* kbar, uint16_t* vbar, uint16_t* krbar_route, float* krbar_norm, void* stream) {
   if (!x || !w_k || !w_v || !w_kr || !w_norm || !doc_tok_off || !doc_blk_off || !kbar || !vbar || !krbar_route)
     return fail(MSA_ERR_NULL, "msa_encode_blocks: null pointer");
-  if (n_layers < 1 || H < 64 || H % 64 != 0 || n_tok < 1 || n_docs < 1 || n_blk < 0 || !(eps >= 0.f) ||
+  if (n_layers < 1 || H < 128 || H % 128 != 0 || n_tok < 1 || n_docs < 1 || n_blk < 0 || !(eps >= 0.f) ||
       !(theta > 0.f))
     return fail(MSA_ERR_SHAPE, "msa_encode_blocks: n_layers=%d H=%d n_tok=%lld n_docs=%d n_blk=%lld", n_layers, H,
                 (long long)n_tok, n_docs, (long long)n_blk);

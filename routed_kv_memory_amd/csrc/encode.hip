@@ -14,20 +14,22 @@
 // row j, k 8 g .. 8 g + 7 -- is 16 contiguous bytes per lane in either operand.
 //
 // Work: one 512-thread workgroup per (4 consecutive blocks = 256 token rows, pair of
-// output heads = 256 columns of K, V or Kr).  The hidden dimension is walked in 64-wide
-// chunks staged in LDS in fragment order (each fragment 1 KiB, lane-major, so both the
-// staging stores and the operand reads are contiguous per wave): 32 row fragments and
-// 32 column fragments per chunk, two stages of 64 KiB.  Each wave loads 8 of the
-// chunk's fragments into registers one chunk ahead and stores them after computing the
-// current chunk, so a single barrier per chunk orders everything.  Wave (wr, wc)
-// accumulates block wr (64 rows) x head wc of the pair (128 columns): 4 x 8 accumulator
-// tiles, kept in VGPRs (the library is built with MFMA's VGPR form).  The epilogue stays in registers: a row's 128
-// columns sit in the 16 lanes of a DPP row (per-row mean square by a row reduction),
-// columns e and e + 64 of a head are in the same lane (the rotation needs no exchange),
-// and a block mean is an in-lane sum over 16 rows plus a sum over the 4 lane groups.
-// The 12 head pairs of a row group are placed on one XCD, so its L2 serves their
-// common hidden rows.  Rows past a block's end (or the last token) are loaded from a
-// clamped, in-bounds row and never enter a mean.
+// output heads = 256 columns of K, V or Kr).  The hidden dimension is walked in 32-wide
+// chunks (one MFMA k step); a chunk is 16 row fragments and 16 column fragments of
+// 1 KiB, and it reaches LDS by direct global->LDS loads (global_load_lds_dwordx4: a
+// wave instruction writes 64 lanes x 16 B contiguously, i.e. exactly one fragment in the
+// lane-major order the operand reads want), through a ring of 4 stages, 3 chunks ahead,
+// with no staging registers.  Each wave loads 4 of a chunk's fragments and waits for its
+// own loads of a chunk before the barrier that publishes it; the barrier also retires
+// every wave's reads of the stage the next loads overwrite.  Wave (wr, wc) accumulates
+// block wr (64 rows) x head wc of the pair (128 columns): 4 x 8 accumulator tiles, kept
+// in VGPRs (the library is built with MFMA's VGPR form).  The epilogue stays in
+// registers: a row's 128 columns sit in the 16 lanes of a DPP row (per-row mean square by
+// a row reduction), columns e and e + 64 of a head are in the same lane (the rotation
+// needs no exchange), and a block mean is an in-lane sum over 16 rows plus a sum over the
+// 4 lane groups.  Workgroups are placed so that those an XCD runs together share 4 head
+// pairs' weights and 8 row groups' hidden rows through its L2.  Rows past a block's end (or the last token) are
+// loaded from a clamped, in-bounds row and never enter a mean.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -36,8 +38,12 @@ namespace {
 
 constexpr int kEncBlocks = 4;                  // blocks per workgroup (= 256 token rows)
 constexpr int kPairs = 3 * kHeads / 2;         // head pairs: K 0-3, V 4-7, Kr 8-11
-constexpr int kKC = 64;                        // hidden columns per staged chunk
-constexpr int kFrags = 64;                     // fragments per chunk: 2 k halves x (16 row + 16 column)
+constexpr int kKC = 64;                        // hidden columns per staged chunk (128 B of a row)
+constexpr int kRegionKB = 32;                  // per chunk: 256 rows (or columns) x 128 B = 32 KiB
+constexpr int kLoadsPerChunk = 8;              // direct-to-LDS loads per wave per chunk
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
+// everything retired
+constexpr int kWaitAll = 0;
 constexpr double kInv2Pi = 0.15915494309189533577;
 
 __device__ __forceinline__ int32_t find_doc(const int64_t* __restrict__ off, int32_t n, int64_t x) {
@@ -56,18 +62,28 @@ encode_kernel(int32_t H, const uint16_t* __restrict__ x, int64_t n_tok, const ui
               const int64_t* __restrict__ tok_off, const int64_t* __restrict__ blk_off, int32_t n_docs,
               int64_t n_blk, int64_t tiles, int64_t n_groups, uint16_t* __restrict__ kbar,
               uint16_t* __restrict__ vbar, uint16_t* __restrict__ krt, float* __restrict__ krn) {
-  // stage[buf][f][lane]: fragment f of the chunk (f = 16 h + mt for rows, 32 + 16 h + nt for
-  // columns, h the 32-wide half of the chunk), lane-major
-  __shared__ u32x4 stage[2][kFrags * 64];
+  // two stages of one chunk each: rows region (32 KiB) then columns region (32 KiB).  Inside a
+  // region, load d (d = 0..31) holds rows 8 d .. 8 d + 7: lane l of the load holds 16-byte
+  // segment (l & 7) ^ (l >> 3) of row 8 d + (l >> 3), i.e. row r' = l >> 3 keeps its eight
+  // segments XOR-permuted by r', so the loads read whole 128-byte lines and the fragment reads
+  // (16 rows, one segment each) spread over all banks.  Two arrays, so that the compiler
+  // sees which stage each access touches.
+  __shared__ u32x4 stage0[2 * kRegionKB * 64], stage1[2 * kRegionKB * 64];
   __shared__ int64_t s_t0[kEncBlocks], s_pos[kEncBlocks];
   __shared__ int32_t s_n[kEncBlocks];
 
-  // XCD-aware placement: the 12 head pairs of a row group share the XCD of the group
+  // XCD-aware placement (workgroup i runs on XCD i % 8).  An XCD takes the row groups
+  // grp = 8 r + xcd; its workgroups come in runs of 32 (about what its 32 CUs hold at once)
+  // covering 8 of its row groups x 4 head pairs of one output, so that while they run
+  // together each pair's weights are read by 8 workgroups and each row group's hidden rows
+  // by 4, from the XCD's L2.  The three outputs' runs over the same 8 row groups follow
+  // each other.
   const int64_t i = blockIdx.x;
   const int xcd = (int)(i & 7);
   const int64_t slot = i >> 3;
-  const int64_t grp = (slot / kPairs) * 8 + xcd;
-  const int pair = (int)(slot % kPairs);
+  const int64_t run = slot / 32, within = slot % 32;
+  const int64_t grp = ((run / 3) * 8 + within / 4) * 8 + xcd;
+  const int pair = (int)((run % 3) * 4 + within % 4);
   if (grp >= n_groups) return;                 // uniform
   const int out = pair / 4;                    // 0 K, 1 V, 2 Kr
   const int head0 = 2 * (pair % 4);
@@ -97,43 +113,43 @@ encode_kernel(int32_t H, const uint16_t* __restrict__ x, int64_t n_tok, const ui
   }
   __syncthreads();
 
-  // this wave stages row fragments mt = wave, wave + 8 (row 16 (wave & 3) + j of blocks
-  // wave >> 2 and 2 + (wave >> 2)) and column fragments nt = wave, wave + 8 (column
-  // 16 wave + j of heads head0 and head0 + 1), both k halves: 8 fragments per chunk
-  const uint16_t* xrow[2];
-  const uint16_t* wrow[2];
+  // this wave's loads: d = wave + 8 q (q = 0..3) of the rows region (token rows 8 d + (lane >> 3))
+  // and of the columns region (output columns 8 d + (lane >> 3) of the pair)
+  const int seg = (lane & 7) ^ ((lane >> 3) & 7);
+  const uint16_t* xrow[4];
+  const uint16_t* wrow[4];
   {
     const uint16_t* xl = x + layer * n_tok * (int64_t)H;
     const uint16_t* wsel = out == 0 ? w_k : (out == 1 ? w_v : w_kr);
     const uint16_t* wl = wsel + layer * (int64_t)kRow * H;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      int64_t t = s_t0[2 * q + (wave >> 2)] + 16 * (wave & 3) + j;
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * (wave + 8 * q) + (lane >> 3);      // 0..255
+      int64_t t = s_t0[r >> 6] + (r & 63);
       if (t > n_tok - 1) t = n_tok - 1;
-      xrow[q] = xl + t * (int64_t)H + 8 * g;
-      const int col = (head0 + q) * kDim + 16 * wave + j;
-      wrow[q] = wl + (int64_t)col * H + 8 * g;
+      xrow[q] = xl + t * (int64_t)H + 8 * seg;
+      const int col = (head0 + (r >> 7)) * kDim + (r & 127);
+      wrow[q] = wl + (int64_t)col * H + 8 * seg;
     }
   }
-
-  uint4 pf[8];
-  auto issue = [&](int kc) {
+  typedef __attribute__((address_space(1))) const void* gptr_t;
+  typedef __attribute__((address_space(3))) void* lptr_t;
+  auto stage_of = [&](int st) -> u32x4* { return st == 0 ? stage0 : stage1; };   // st constant after unrolling
+  auto issue = [&](int c, int st) {          // chunk c -> stage st = c % 2
+    u32x4* sp = stage_of(st);
+    const int kc = c * kKC;
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        pf[2 * q + h] = *reinterpret_cast<const uint4*>(xrow[q] + kc + 32 * h);
-        pf[4 + 2 * q + h] = *reinterpret_cast<const uint4*>(wrow[q] + kc + 32 * h);
-      }
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_global_load_lds((gptr_t)(xrow[q] + kc), (lptr_t)(sp + (wave + 8 * q) * 64), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)(wrow[q] + kc), (lptr_t)(sp + (kRegionKB + wave + 8 * q) * 64),
+                                       16, 0, 0);
+    }
   };
-  auto commit = [&](int b) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        stage[b][(16 * h + wave + 8 * q) * 64 + lane] = __builtin_bit_cast(u32x4, pf[2 * q + h]);
-        stage[b][(32 + 16 * h + wave + 8 * q) * 64 + lane] = __builtin_bit_cast(u32x4, pf[4 + 2 * q + h]);
-      }
+  // fragment (16 rows from row0, k segment s of 8) of a region, as this lane's 16 bytes:
+  // lane (g, j) takes row row0 + j, which sits in load (row0 + j) >> 3 at lane 8 (j & 7) + (s ^ (j & 7))
+  auto frag = [&](const u32x4* region, int row0, int s) {
+    const int r = row0 + j;
+    return __builtin_bit_cast(bf16x8, region[(r >> 3) * 64 + 8 * (j & 7) + (s ^ (j & 7))]);
   };
 
   const int wr = wave & 3, wc = wave >> 2;
@@ -143,34 +159,37 @@ encode_kernel(int32_t H, const uint16_t* __restrict__ x, int64_t n_tok, const ui
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int b) {
+  const int n_chunks = H / kKC;                // even (H % 128 == 0)
+  // one chunk: wait for this wave's loads of it (and lgkmcnt(0): this wave's reads of the other
+  // stage are retired), barrier (chunk c is in its stage for every wave, and every wave is done
+  // reading chunk c - 1), load chunk c + 1 into chunk c - 1's stage, multiply chunk c.  No
+  // branch: past the end the loads repeat the last chunk (never read), so every wait is exact.
+  auto step = [&](int c, int st) {
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    asm volatile("s_barrier" ::: "memory");  // the clobber keeps every LDS access on its side
+    issue(min(c + 1, n_chunks - 1), st ^ 1);
+    __builtin_amdgcn_sched_barrier(0);       // keep the loads ahead of the products (no sinking)
+    const u32x4* sp = stage_of(st);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8 af[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) af[m] = __builtin_bit_cast(bf16x8, stage[b][(16 * h + 4 * wr + m) * 64 + lane]);
+      for (int m = 0; m < 4; ++m) af[m] = frag(sp, 64 * wr + 16 * m, 4 * h + g);
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const bf16x8 bf = __builtin_bit_cast(bf16x8, stage[b][(32 + 16 * h + 8 * wc + n) * 64 + lane]);
+        const bf16x8 bf = frag(sp + kRegionKB * 64, 128 * wc + 16 * n, 4 * h + g);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bf, acc[m][n], 0, 0, 0);
+        for (int m = 0; m < 4; ++m)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bf, acc[m][n], 0, 0, 0);
       }
     }
   };
-  issue(0);
-  commit(0);
-  int buf = 0;
-  // branch-free steady state (the last chunk is peeled): barrier, loads of the next chunk
-  // into registers, the current chunk's products, the next chunk's stores
-  for (int kc = kKC; kc < H; kc += kKC, buf ^= 1) {
-    __syncthreads();   // the chunk before kc is in stage buf; every reader of stage buf ^ 1 is done
-    issue(kc);
-    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the products (no sinking)
-    compute(buf);
-    commit(buf ^ 1);
+  issue(0, 0);
+  for (int c = 0; c < n_chunks; c += 2) {
+    step(c, 0);
+    step(c + 1, 1);
   }
-  __syncthreads();
-  compute(buf);
+  __builtin_amdgcn_s_waitcnt(kWaitAll);        // the repeated loads land before the LDS is released
 
   // epilogue, row by row: the key's per-row RMS normalisation (the 16 lanes of a DPP row
   // hold the row's 128 columns, 8 per lane), norm weight and rotation of pairs (c, c + 64),
@@ -269,8 +288,8 @@ hipError_t launch_encode(int32_t L, int32_t H, const uint16_t* x, int64_t n_tok,
   if (tiles == 0) return hipSuccess;
   // every block of every tile (padding blocks included, so the route layout is complete)
   const int64_t n_groups = tiles * kTile / kEncBlocks;
-  const int64_t groups8 = (n_groups + 7) / 8 * 8;
-  const dim3 grid((unsigned)(groups8 * kPairs), (unsigned)L);
+  const int64_t groups_per_xcd = ((n_groups + 7) / 8 + 7) / 8 * 8;   // whole runs of 8 row groups
+  const dim3 grid((unsigned)(8 * groups_per_xcd * kPairs), (unsigned)L);
   hipLaunchKernelGGL(encode_kernel, grid, dim3(512), 0, s, H, x, n_tok, w_k, w_v, w_kr, w_norm, eps,
                      log2((double)theta), doc_tok_off, doc_blk_off, n_docs, n_blk, tiles, n_groups, kbar, vbar,
                      krt, krn);

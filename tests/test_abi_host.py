@@ -98,15 +98,15 @@ def test_invalid_arguments_are_rejected_on_the_host(msa):
                                   fake, None) == 2
     assert lib.msa_sparse_prefill(1, 1, 4, 24, fake, fake, fake, fake, 8, fake, fake, fake, 4, ctypes.c_float(0.1),
                                   fake, None) == 3
-    # encode: null, hidden size not a multiple of 64, zero layers, theta 0
+    # encode: null, hidden size not a multiple of 128, zero layers, theta 0
     F = ctypes.c_float
-    assert lib.msa_encode_blocks(1, 64, None, 10, fake, fake, fake, fake, F(1e-6), F(1e6), fake, fake, 1, 1, fake,
+    assert lib.msa_encode_blocks(1, 128, None, 10, fake, fake, fake, fake, F(1e-6), F(1e6), fake, fake, 1, 1, fake,
                                  fake, fake, None, None) == 1
-    assert lib.msa_encode_blocks(1, 96, fake, 10, fake, fake, fake, fake, F(1e-6), F(1e6), fake, fake, 1, 1, fake,
+    assert lib.msa_encode_blocks(1, 192, fake, 10, fake, fake, fake, fake, F(1e-6), F(1e6), fake, fake, 1, 1, fake,
                                  fake, fake, None, None) == 2
-    assert lib.msa_encode_blocks(0, 64, fake, 10, fake, fake, fake, fake, F(1e-6), F(1e6), fake, fake, 1, 1, fake,
+    assert lib.msa_encode_blocks(0, 128, fake, 10, fake, fake, fake, fake, F(1e-6), F(1e6), fake, fake, 1, 1, fake,
                                  fake, fake, None, None) == 2
-    assert lib.msa_encode_blocks(1, 64, fake, 10, fake, fake, fake, fake, F(1e-6), F(0.0), fake, fake, 1, 1, fake,
+    assert lib.msa_encode_blocks(1, 128, fake, 10, fake, fake, fake, fake, F(1e-6), F(0.0), fake, fake, 1, 1, fake,
                                  fake, fake, None, None) == 2
     # workspace too small
     need = lib.msa_route_topk_workspace_size(2, 1, 100000, 16)

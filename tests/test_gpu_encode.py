@@ -89,11 +89,11 @@ def check_layerwise(x, w, wn, eps, theta, tok, with_norms=True):
 
 def test_ragged_documents_all_outputs():
     """Documents of 1, 63, 64, 65 tokens, an empty one, and longer ones; two layers."""
-    print("case: encode ragged H=192", flush=True)
+    print("case: encode ragged H=384", flush=True)
     rng = np.random.default_rng(301)
     lens = np.array([1, 63, 64, 65, 0, 130, 200, 7, 640, 129])
     tok = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
-    L, Hd = 2, 192
+    L, Hd = 2, 384
     x = S.f32_to_bf16(rng.standard_normal((L, int(tok[-1]), Hd)).astype(np.float32))
     w, wn = make_weights(rng, L, Hd)
     check_layerwise(x, w, wn, 1e-6, 1e6, tok)
@@ -116,7 +116,7 @@ def test_long_document_positions(theta):
     print("case: encode long document theta=%g" % theta, flush=True)
     rng = np.random.default_rng(303)
     tok = np.array([0, 5, 12005], np.int64)
-    L, Hd = 1, 64
+    L, Hd = 1, 128
     x = S.f32_to_bf16(rng.standard_normal((L, 12005, Hd)).astype(np.float32))
     w, wn = make_weights(rng, L, Hd)
     check_layerwise(x, w, wn, 1e-6, theta, tok)
@@ -127,7 +127,7 @@ def test_zero_rows_use_eps():
     print("case: encode zero rows", flush=True)
     rng = np.random.default_rng(304)
     tok = np.array([0, 70, 140], np.int64)
-    L, Hd = 1, 64
+    L, Hd = 1, 128
     x = S.f32_to_bf16(rng.standard_normal((L, 140, Hd)).astype(np.float32))
     x[0, :70] = 0
     w, wn = make_weights(rng, L, Hd)
