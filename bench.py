@@ -41,8 +41,8 @@ SCAN_TRAFFIC_SOURCE_DIGEST = "c5efc6a8e7e028e0cb0ad7ace550b61865b4074a042a374efa
 # HBM traffic of one encode launch (18 layers, 1M-token document set), FETCH_SIZE + WRITE_SIZE
 # passes scaled by the 1 GiB calibration copy, recorded in profiles/encode_1m_tokens.md; valid for
 # the kernel source it was measured on only.
-ENCODE_TRAFFIC_BYTES = 1259.8e9
-ENCODE_TRAFFIC_SOURCE_DIGEST = "0885938f6f19547c7d79c5bf2f57bca659daa8431d591b0767d1b943db2c9705"
+ENCODE_TRAFFIC_BYTES = 537.0e9
+ENCODE_TRAFFIC_SOURCE_DIGEST = "d3a5447ca4f6a8279b81a57fb83cace06f7218f2083d2d519cfb41dd0c84aa39"
 
 
 def source_digest(files=("route.hip", "msa_device.hpp")):

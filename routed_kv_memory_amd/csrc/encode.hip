@@ -38,6 +38,11 @@ namespace {
 
 constexpr int kEncBlocks = 4;                  // blocks per workgroup (= 256 token rows)
 constexpr int kPairs = 3 * kHeads / 2;         // head pairs: K 0-3, V 4-7, Kr 8-11
+#ifndef MSA_ENCODE_RUN_PAIRS
+#define MSA_ENCODE_RUN_PAIRS 4
+#endif
+constexpr int kRunPairs = MSA_ENCODE_RUN_PAIRS;   // head pairs in a run of 32 workgroups on one XCD
+constexpr int kRunGroups = 32 / kRunPairs;        // row groups in a run
 constexpr int kKC = 64;                        // hidden columns per staged chunk (128 B of a row)
 constexpr int kRegionKB = 32;                  // per chunk: 256 rows (or columns) x 128 B = 32 KiB
 constexpr int kLoadsPerChunk = 8;              // direct-to-LDS loads per wave per chunk
@@ -82,8 +87,8 @@ encode_kernel(int32_t H, const uint16_t* __restrict__ x, int64_t n_tok, const ui
   const int xcd = (int)(i & 7);
   const int64_t slot = i >> 3;
   const int64_t run = slot / 32, within = slot % 32;
-  const int64_t grp = ((run / 3) * 8 + within / 4) * 8 + xcd;
-  const int pair = (int)((run % 3) * 4 + within % 4);
+  const int64_t grp = ((run / (kPairs / kRunPairs)) * kRunGroups + within / kRunPairs) * 8 + xcd;
+  const int pair = (int)((run % (kPairs / kRunPairs)) * kRunPairs + within % kRunPairs);
   if (grp >= n_groups) return;                 // uniform
   const int out = pair / 4;                    // 0 K, 1 V, 2 Kr
   const int head0 = 2 * (pair % 4);
@@ -288,7 +293,7 @@ hipError_t launch_encode(int32_t L, int32_t H, const uint16_t* x, int64_t n_tok,
   if (tiles == 0) return hipSuccess;
   // every block of every tile (padding blocks included, so the route layout is complete)
   const int64_t n_groups = tiles * kTile / kEncBlocks;
-  const int64_t groups_per_xcd = ((n_groups + 7) / 8 + 7) / 8 * 8;   // whole runs of 8 row groups
+  const int64_t groups_per_xcd = ((n_groups + 7) / 8 + kRunGroups - 1) / kRunGroups * kRunGroups;   // whole runs
   const dim3 grid((unsigned)(8 * groups_per_xcd * kPairs), (unsigned)L);
   hipLaunchKernelGGL(encode_kernel, grid, dim3(512), 0, s, H, x, n_tok, w_k, w_v, w_kr, w_norm, eps,
                      log2((double)theta), doc_tok_off, doc_blk_off, n_docs, n_blk, tiles, n_groups, kbar, vbar,
