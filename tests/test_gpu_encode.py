@@ -134,3 +134,49 @@ def test_zero_rows_use_eps():
     blk, n_blk, kbar, vbar, krt, krn = run_encode(x, w, wn, 1e-6, 1e6, tok)
     assert np.all(u16(kbar)[0, :2] == 0) and np.all(u16(vbar)[0, :2] == 0)
     check_layerwise(x, w, wn, 1e-6, 1e6, tok)
+
+
+def test_full_size_encode_sampled():
+    """The encode workload at its full size and in bench.py's launch configuration (18 layers x
+    947,395 tokens x hidden 2,560, one launch): sampled blocks against the oracle -- the key of
+    documents' first blocks (positions 0..63), value and routing key of blocks anywhere (they do
+    not depend on position) -- plus the stored routing-key norms of whole tiles."""
+    print("case: encode full size (18 x 947,395 x 2,560)", flush=True)
+    from synth.device import DeviceInputs
+    torch.cuda.empty_cache()
+    cfg = S.CONFIGS["1m"]
+    Hd, eps, theta = S.ENC_HIDDEN, 1e-6, 1e6
+    tok, x, wk, wv, wr, wn = DeviceInputs(cfg, DEV).encode_inputs(Hd)
+    L, n_tok = x.shape[0], x.shape[1]
+    blk, n_blk, _ = msa.msa_block_offsets_host(tok)
+    kbar = torch.empty((L, n_blk, 8, 128), dtype=torch.bfloat16, device=DEV)
+    vbar = torch.empty_like(kbar)
+    krt, krn = alloc_route_keys(L, n_blk)
+    msa.msa_encode_blocks(x, wk, wv, wr, wn, eps, theta, tok.to(DEV), blk.to(DEV), n_blk, kbar, vbar, krt, krn)
+    torch.cuda.synchronize()
+    del x
+    seed = S.memory_config(cfg).seed
+    tok_n, blk_n = tok.numpy(), blk.numpy()
+    rng = np.random.default_rng(71)
+    wn_h = u16(wn)
+    for l in (0, 9, L - 1):
+        w_h = [np.ascontiguousarray(S.enc_weights_host(seed, st, l, Hd).T)
+               for st in (S.S_ENC_WK, S.S_ENC_WV, S.S_ENC_WKR)]
+        d = int(rng.integers(0, tok_n.size - 1))
+        nb = int(blk_n[d + 1] - blk_n[d])
+        for jb, keys in ((0, "KVR"), (int(rng.integers(0, nb)), "VR"), (nb - 1, "VR")):
+            t0 = int(tok_n[d]) + 64 * jb
+            t1 = min(t0 + 64, int(tok_n[d + 1]))
+            xh = S.enc_x_host(seed, l, n_tok, Hd, t0, t1)
+            ref = O.encode(xh, *w_h, wn_h[l], eps, theta, np.array([0, t1 - t0], np.int64),
+                           np.array([0, 1], np.int64))
+            b = int(blk_n[d]) + jb
+            got = {"K": u16(kbar[l, b]), "V": u16(vbar[l, b]),
+                   "R": untile_keys(krt[l:l + 1, 16 * (b // 16):16 * (b // 16) + 16], 16)[0, b % 16]}
+            for key, r in zip("KVR", ref):
+                if key in keys:
+                    assert_pooled_close(got[key][None], r, "%s layer %d doc %d block %d" % (key, l, d, jb))
+    # stored norms of the routing keys, two whole layers
+    for l in (0, L - 1):
+        rows = untile_keys(krt[l:l + 1], n_blk)
+        assert np.allclose(untile_norms(krn[l:l + 1], n_blk), O.head_norms(rows), rtol=1e-6, atol=0)
