@@ -120,9 +120,11 @@ prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint
     }
   };
 
-  // Scores are kept in log2 units (scale folded with log2 e).  The running maximum is
-  // raised only when a tile exceeds it by more than kSlack, so unnormalised
-  // probabilities stay below 2^kSlack and the accumulators are rescaled rarely.
+  // The running maximum is kept in log2 units (scale folded with log2 e): each raw score s
+  // enters exp2 as one fma(s, scale2, -m), and the tile maximum is taken over raw scores
+  // (scale2 > 0 keeps the order).  The maximum is raised only when a tile exceeds it by more
+  // than kSlack, so unnormalised probabilities stay below 2^kSlack and the accumulators are
+  // rescaled rarely.
   constexpr float kSlack = 8.f;
   const float scale2 = scale * 1.4426950408889634f;
   float m_run[HPW], l_lane[HPW];
@@ -170,16 +172,13 @@ prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint
       bf16x8 pfh[HPW], pfl[HPW];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        // scale to log2 units and mask (tiles every token of the block sees whole need no mask)
+        // mask (tiles every token of the block sees whole need none), raw maximum
         float mt = ninf;
         if (whole) {
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              sc[hh][h2][r] *= scale2;
-              mt = fmaxf(mt, sc[hh][h2][r]);
-            }
+            for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc[hh][h2][r]);
         } else {
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2)
@@ -187,12 +186,12 @@ prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint
             for (int r = 0; r < 4; ++r) {
               const int32_t key = k0 + 16 * h2 + 4 * g + r;
               const bool ok = key < n_keys && (key < clen || key - clen < vis_tok);
-              const float v = ok ? sc[hh][h2][r] * scale2 : ninf;
+              const float v = ok ? sc[hh][h2][r] : ninf;
               sc[hh][h2][r] = v;
               mt = fmaxf(mt, v);
             }
         }
-        mt = rows4_max(mt);                    // over the tile's 32 keys of token t0 + j
+        mt = rows4_max(mt) * scale2;           // over the tile's 32 keys of token t0 + j, log2 units
         // raise the reference maximum only past the slack (ballot: most tiles skip the rescale)
         const bool raise = mt > m_run[hh] + kSlack;
         if (__ballot(raise)) {
@@ -203,17 +202,15 @@ prefill_kernel(int32_t T, int32_t Hq, const uint16_t* __restrict__ q, const uint
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) o[hh][dt] *= alpha;
         }
-        const float m_use = m_run[hh] == ninf ? 0.f : m_run[hh];   // a token with no visible key yet
-        float psum = 0.f;
+        const float neg_m = m_run[hh] == ninf ? 0.f : -m_run[hh];   // a token with no visible key yet
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = __builtin_amdgcn_exp2f(sc[hh][h2][r] - m_use);
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hh][h2][r], scale2, neg_m));
             sc[hh][h2][r] = p;
-            psum += p;
+            l_lane[hh] += p;
           }
-        l_lane[hh] += psum;
         // P^T as the B operand: k slot 8 g + e holds key 4 g + e (e < 4) or 16 + 4 g + e - 4.
         // P = P_hi + P_lo with both parts in bf16 (two products), so the probabilities
         // enter the matrix cores with ~16 significant bits rather than 8.
