@@ -258,6 +258,30 @@ def test_gather_decode_edges(Hq):
     assert int(cl1.cpu()[0, 0]) == 0 and bool((z == 0).all())
 
 
+@pytest.mark.parametrize("Hq", [8, 64])
+def test_decode_row_count_boundaries(Hq):
+    """Total row counts around the 32-row wave and 128-row split boundaries, with the memory /
+    local seam inside a wave's rows."""
+    print("case: decode boundaries Hq=%d" % Hq, flush=True)
+    rng = np.random.default_rng(29 + Hq)
+    totals = [1, 31, 32, 33, 127, 128, 129, 255, 256, 257]
+    L, B = 1, len(totals)
+    max_ctx, max_loc = 160, 160
+    ck, cv = rand_bf16(rng, (L, B, max_ctx, 8, 128)), rand_bf16(rng, (L, B, max_ctx, 8, 128))
+    lk, lv = rand_bf16(rng, (L, B, max_loc, 8, 128)), rand_bf16(rng, (L, B, max_loc, 8, 128))
+    q = rand_bf16(rng, (L, B, Hq, 128))
+    cl = np.array([[min(t // 2 + 3, t, max_ctx) for t in totals]], np.int32)
+    ll = np.array([[t - c for t, c in zip(totals, cl[0])]], np.int32)
+    assert (ll <= max_loc).all()
+    out = decode_all(to_dev_bf16(q), to_dev_bf16(ck), to_dev_bf16(cv), torch.from_numpy(cl).to(DEV),
+                     to_dev_bf16(lk), to_dev_bf16(lv), torch.from_numpy(ll).to(DEV))
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = O.decode(q[0, b], ck[0, b, :cl[0, b]], cv[0, b, :cl[0, b]], lk[0, b, :ll[0, b]], lv[0, b, :ll[0, b]],
+                       SCALE)
+        assert_decode(out.cpu().numpy()[0, b], ref)
+
+
 def test_decode_long_context_many_splits():
     print("case: decode long context", flush=True)
     rng = np.random.default_rng(17)
