@@ -273,13 +273,27 @@ def main():
     if cfg.per_token:
         rows["A1_pool"] = hbm_row(float(seg_mean[0]), L * n_tok * POOL_BYTES_PER_TOKEN + 3 * L * n_blk * 2048,
                                   "K, V, Kr token rows read + K-bar, V-bar, Kr-bar rows written")
-    rows["A2_route_scan"] = dict(roofline, ms=round(scan_ms, 4))
+    LLC_BYTES = 256e6                     # MI355X last-level (Infinity) cache
+    scan_bytes = L * n_blk * SCAN_BYTES_PER_BLOCK_LAYER
+    if cfg.per_token:
+        scan_cache = ("keys written by the pooling earlier in the step (%.2f GB): the part still in the "
+                      "%d MB last-level cache is served from it" % (scan_bytes / 1e9, LLC_BYTES / 1e6))
+    else:
+        scan_cache = ("cold: %.1f GB of keys stream through the %d MB last-level cache"
+                      % (scan_bytes / 1e9, LLC_BYTES / 1e6))
+    rows["A2_route_scan"] = dict(roofline, ms=round(scan_ms, 4), cache=scan_cache)
     rows["A3_topk"] = dict(hbm_row(float(seg_mean[2]), L * B * n_docs * 4 + L * B * k * 8, "scores read + ids/scores written"),
                            bound="latency (%d rows of %d scores)" % (L * B, n_docs))
     rows["A4_gather"] = dict(hbm_row(float(seg_mean[3]), ctx_rows * 4 * 2048, "K-bar and V-bar rows read + written"),
                              bound="latency (dependent id -> offset -> row loads)")
+    loc_bytes = L * B * cfg.L_loc * DECODE_BYTES_PER_ROW
+    other = scan_bytes + (L * n_tok * POOL_BYTES_PER_TOKEN if cfg.per_token else 0)
     rows["A5_decode"] = dict(hbm_row(float(seg_mean[4]), dec_rows * DECODE_BYTES_PER_ROW, "K and V rows of 8 heads read"),
-                             bound="hbm")
+                             bound="hbm",
+                             cache="memory context (%.1f MB) written by the gather just before: warm; local rows "
+                                   "(%.0f MB) last touched a step earlier, behind %.2f GB of other traffic: %s"
+                                   % (ctx_rows * 2048 * 2 / 1e6, loc_bytes / 1e6, other / 1e9,
+                                      "cold" if other + loc_bytes > LLC_BYTES else "cache-resident"))
     result["rows"] = rows
     if not args.no_cpu_baseline:
         result["cpu_rows"] = cpu_rows(cfg, L, B, k, n_docs, blk.numpy(), dsc, ids, kbar, vbar, q, ck, cv, cl, lk,
