@@ -34,8 +34,8 @@ POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 # WRITE_SIZE rocprofv3 passes (scaled by a 1 GiB calibration kernel) recorded in
 # profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
 # sources' digest differs, the figure is stale and bench.py reports null.
-SCAN_TRAFFIC_BYTES = 57.694e9
-SCAN_TRAFFIC_SOURCE_DIGEST = "c5efc6a8e7e028e0cb0ad7ace550b61865b4074a042a374efa7a5a846274a6fd"
+SCAN_TRAFFIC_BYTES = 57.693e9
+SCAN_TRAFFIC_SOURCE_DIGEST = "fd4bd8a73e4928f56399b7176b8d167b71ef3de9bbc70ea388e3abeac35ba0d0"
 
 
 # HBM traffic of one encode launch (18 layers, 1M-token document set), FETCH_SIZE + WRITE_SIZE

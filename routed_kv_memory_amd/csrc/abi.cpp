@@ -50,6 +50,20 @@ DeviceInfo device_info() {
   return DeviceInfo{cached_cus[dev]};
 }
 
+int stream_cus(hipStream_t s) {
+  const int dev_cus = device_info().cus;
+  uint32_t mask[32] = {0};                       // up to 1,024 CUs
+  const uint32_t words = (uint32_t)((dev_cus + 31) / 32);
+  if (words > 32) return dev_cus;
+  if (hipExtStreamGetCUMask(s, words, mask) != hipSuccess) {
+    (void)hipGetLastError();                     // not a launch error: leave no sticky status behind
+    return dev_cus;
+  }
+  int n = 0;
+  for (uint32_t w = 0; w < words; ++w) n += __builtin_popcount(mask[w]);
+  return n > 0 && n < dev_cus ? n : dev_cus;
+}
+
 }  // namespace msa
 
 MSA_API int msa_abi_version(void) { return MSA_ABI_VERSION; }

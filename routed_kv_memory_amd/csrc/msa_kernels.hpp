@@ -11,6 +11,10 @@ struct DeviceInfo {
   int cus;       // compute units
 };
 DeviceInfo device_info();
+// CUs a stream may run on: the popcount of its CU mask (all of the device's CUs for an
+// unmasked stream).  Persistent grids are sized by it, so a scan on a CU-masked stream fills
+// exactly the CUs it was given and leaves the others to work on other streams.
+int stream_cus(hipStream_t s);
 
 inline int64_t route_tiles(int64_t n_blk) { return (n_blk + 15) / 16; }
 

@@ -482,15 +482,15 @@ hipError_t launch_route_scores(int32_t L, const uint16_t* qr, int32_t B, int32_t
   const int64_t tiles = route_tiles(n_blk);
   const int64_t n_codes = (int64_t)L * B * n_docs;
   uint32_t* codes = reinterpret_cast<uint32_t*>(doc_scores);
-  const DeviceInfo di = device_info();
-  const int fill_grid = (int)((n_codes + 255) / 256 < di.cus * 4 ? (n_codes + 255) / 256 : di.cus * 4);
+  const int cus = stream_cus(s);                 // the persistent grid fills the stream's CUs
+  const int fill_grid = (int)((n_codes + 255) / 256 < cus * 4 ? (n_codes + 255) / 256 : cus * 4);
 
   hipLaunchKernelGGL(codes_init_kernel, dim3(fill_grid), dim3(256), 0, s, codes, n_codes, accumulate);
   if (tiles > 0) {
     if (T >= 16) {
       const int n_tc = (T + kTokChunk - 1) / kTokChunk;
       const int C = B * n_tc;
-      const int R = choose_ranges(C, di.cus);
+      const int R = choose_ranges(C, cus);
       const int NT = T >= kTokChunk ? 4 : (T + 15) / 16;
       const dim3 grid((unsigned)(R * C));
       const uint4* kt = reinterpret_cast<const uint4*>(krt);

@@ -92,3 +92,40 @@ def test_every_entry_point_is_deterministic():
     for i, (x, y) in enumerate(zip(a, b)):
         assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y), i
+
+
+def test_scan_on_a_cu_masked_stream_matches():
+    """A scan launched on a CU-masked stream sizes its persistent grid to that stream's CUs and
+    gives exactly the scores of an unmasked launch (single query and shared-range cases)."""
+    print("case: scan on a CU-masked stream", flush=True)
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (cus + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for b in range(cus):
+        if b % 32 >= 4:                                   # drop 4 of every 32 CUs
+            mask[b // 32] |= 1 << (b % 32)
+    handle = ctypes.c_void_p()
+    assert hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), ctypes.c_uint32(words), mask) == 0
+    masked = torch.cuda.ExternalStream(handle.value)
+    rng = np.random.default_rng(41)
+    cfg = S.CONFIGS["tiny"]
+    di = DeviceInputs(cfg, DEV)
+    tok, k, v, kr = di.per_token()
+    blk, n_blk, _ = msa.msa_block_offsets_host(tok)
+    L = cfg.n_layers
+    krt, krn = alloc_route_keys(L, n_blk)
+    kbar = torch.empty((L, n_blk, 8, 128), dtype=torch.bfloat16, device=DEV)
+    vbar = torch.empty_like(kbar)
+    blk_d = blk.to(DEV)
+    msa.msa_pool_blocks(k, v, kr, tok.to(DEV), blk_d, n_blk, kbar, vbar, krt, krn)
+    torch.cuda.synchronize()
+    for B, T in ((1, 64), (5, 130)):
+        qr = to_dev_bf16(S.f32_to_bf16(rng.standard_normal((L, B, T, 8, 128)).astype(np.float32)))
+        _, _, d_ref = route(qr, krt, krn, n_blk, blk_d, 4)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(masked):
+            _, _, d_msk = route(qr, krt, krn, n_blk, blk_d, 4)
+        torch.cuda.synchronize()
+        assert torch.equal(d_ref, d_msk), (B, T)
