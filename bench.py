@@ -35,7 +35,7 @@ POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 # profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
 # sources' digest differs, the figure is stale and bench.py reports null.
 SCAN_TRAFFIC_BYTES = 57.693e9
-SCAN_TRAFFIC_SOURCE_DIGEST = "fd4bd8a73e4928f56399b7176b8d167b71ef3de9bbc70ea388e3abeac35ba0d0"
+SCAN_TRAFFIC_SOURCE_DIGEST = "4494e72ddab2cdff98e1c1fbb143dabe59a979bec1dbe7a81edc89b5ae597860"
 
 
 # HBM traffic of one encode launch (18 layers, 1M-token document set), FETCH_SIZE + WRITE_SIZE
@@ -70,11 +70,64 @@ def calibration_copy(dev="cuda"):
     return 1 << 30
 
 
+_CONTIGUOUS = []     # (pointer, bytes) of the key memory allocated by route_key_memory
+
+
+def route_key_memory(shape, dtype):
+    """Device memory for a resident memory bank's routing keys (or their norms): one physically
+    contiguous allocation (hipExtMallocWithFlags, hipDeviceMallocContiguous), wrapped as a tensor
+    and kept until the process ends.  The scan over the 100M-token memory ran ~4% faster from such
+    an allocation than from the caching allocator's, with the same steady rate in every process.
+    Falls back to torch.empty (returned with False) if the runtime refuses."""
+    import ctypes
+
+    import torch
+    itemsize = torch.empty((), dtype=dtype).element_size()
+    nbytes = itemsize
+    for d in shape:
+        nbytes *= d
+    hip = ctypes.CDLL("libamdhip64.so")
+    ptr = ctypes.c_void_p()
+    if nbytes == 0 or hip.hipExtMallocWithFlags(ctypes.byref(ptr), ctypes.c_size_t(nbytes), ctypes.c_uint(0x4)) != 0:
+        hip.hipGetLastError()
+        return torch.empty(shape, dtype=dtype, device="cuda"), False
+    _CONTIGUOUS.append((ptr.value, nbytes))
+    typestr = {1: "|u1", 2: "<i2", 4: "<i4", 8: "<i8"}[itemsize]
+
+    class _Mem:
+        __cuda_array_interface__ = {"shape": tuple(shape), "typestr": typestr, "data": (ptr.value, False),
+                                    "version": 2, "strides": None}
+    return torch.as_tensor(_Mem(), device="cuda").view(dtype), True
+
+
+def warm_up(step, args):
+    """Untimed warm-up: exactly --warmup steps if given, else at least 3 steps and at least
+    --warmup-seconds of them.  Sets args.warmup to the count run (reported in the JSON line)."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while True:
+        if args.warmup is not None and n >= args.warmup:
+            break
+        if args.warmup is None and n >= 3:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= args.warmup_seconds:
+                break
+        step()
+        n += 1
+    torch.cuda.synchronize()
+    args.warmup = n
+    return n
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 3 and at least --warmup-seconds of them)")
+    ap.add_argument("--warmup-seconds", type=float, default=1.5,
+                    help="with no --warmup: keep warming up this long; the scan ran up to 7%% slower in a "
+                         "process's first second of sustained load than afterwards")
     ap.add_argument("--workload", default="100m", choices=["tiny", "1m", "10m", "100m", "prefill", "interleaved", "host-tier", "encode"],
                     help="prefill: the multi-token sparse prefill alone at the interleaved workload's last "
                          "round (18 layers x 8 queries x 1,088 tokens); encode: the offline encode front-end "
@@ -134,8 +187,8 @@ def main():
     n_docs = blk.numel() - 1
     blk_d = blk.to(dev)
     tiles = msa.msa_route_tiles(n_blk)
-    krt = torch.empty((L, tiles * 16, 8, 128), dtype=torch.bfloat16, device=dev)
-    krn = torch.empty((L, tiles * 16, 8), dtype=torch.float32, device=dev)
+    krt, contiguous = route_key_memory((L, tiles * 16, 8, 128), torch.bfloat16)
+    krn, _ = route_key_memory((L, tiles * 16, 8), torch.float32)
     if cfg.per_token:
         kbar = torch.empty((L, n_blk, 8, 128), dtype=torch.bfloat16, device=dev)
         vbar = torch.empty_like(kbar)
@@ -165,6 +218,9 @@ def main():
     print("bench: %s memory ready in %.1f s (%d blocks x %d layers, %d docs, %.1f GB on device)"
           % (cfg.name, t_setup, n_blk, L, n_docs, torch.cuda.memory_allocated() / 1e9), file=sys.stderr, flush=True)
 
+    # The scan reads the key norms when several query chunks make it bound by the matrix
+    # cores; one chunk (bound by HBM) recomputes them from the keys it streams.
+    scan_norms = krn if B * ((T + 63) // 64) > 1 else None
     n_ev = 6
     def step(evs=None):
         rec = (lambda i: evs[i].record()) if evs is not None else (lambda i: None)
@@ -172,7 +228,7 @@ def main():
         if pool_args is not None:
             msa.msa_pool_blocks(*pool_args)
         rec(1)
-        msa.msa_route_scores(qr, krt, n_blk, blk_doc, n_docs, dsc)
+        msa.msa_route_scores(qr, krt, n_blk, blk_doc, n_docs, dsc, krbar_norm=scan_norms)
         rec(2)
         msa.msa_topk_docs(dsc, k, ids, tsc, ws_topk)
         rec(3)
@@ -181,9 +237,7 @@ def main():
         msa.msa_sparse_decode(q, ck, cv, cl, lk, lv, ll, scale, out, ws_dec)
         rec(5)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -210,14 +264,19 @@ def main():
     # The scan does 2*B*T*1024 flop per 2,048-byte key row: below the ridge (peak flop/s over
     # peak B/s, ~312 flop/B) it is bound by HBM, above it by the matrix cores.
     scan_flop = 2.0 * B * T * 1024 * L * n_blk
+    n_chunks = B * ((T + 63) // 64)
+    scan_kernel = ("route_valu_kernel (msa_route_scores)" if T < 16 else
+                   "route_mfma_kernel<%d, %s, %s> (msa_route_scores)"
+                   % (min(4, (T + 15) // 16), "true" if n_chunks == 1 else "false",
+                      "true" if scan_norms is not None else "false"))
     if scan_flop / scan_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
         tflops = scan_flop / (scan_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": "route_mfma_kernel (msa_route_scores)",
+        roofline = {"bound": "mfma", "kernel": scan_kernel,
                     "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                     "algorithmic_flop_per_launch": scan_flop, "hbm_GBps": round(achieved, 2)}
     else:
-        roofline = {"bound": "hbm", "kernel": "route_mfma_kernel (msa_route_scores)",
+        roofline = {"bound": "hbm", "kernel": scan_kernel,
                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": (round(SCAN_TRAFFIC_BYTES / 1e9, 3)
@@ -244,11 +303,15 @@ def main():
             "layers": L, "blocks_per_layer": n_blk, "docs": n_docs, "queries": B, "query_tokens": T,
             "top_k": k, "kv_heads": 8, "head_dim": 128, "q_heads": Hq, "local_rows": cfg.L_loc,
             "route_key_bytes": L * tiles * 16 * 2048, "content_kv_bytes": 2 * L * n_blk * 2048,
+            "route_key_alloc": "one contiguous device allocation" if contiguous else "caching allocator",
+            "scan_key_norms": "read" if scan_norms is not None else "recomputed from the keys",
         },
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "ms_per_query_18_layers": round(ms_step / B, 4),
         "ms_per_query_per_layer": round(ms_step / B / L, 5),
         "scan_ms": round(scan_ms, 4),
+        "scan_ms_median_min_max": [round(float(np.median(seg[:, 1])), 4), round(float(seg[:, 1].min()), 4),
+                                   round(float(seg[:, 1].max()), 4)],
         "scan_ms_per_layer": round(scan_ms / L, 5),
         "blocks_scanned_per_s": round(L * n_blk * B / (scan_ms * 1e-3), 1),
         "breakdown_ms": {"pool": round(float(seg_mean[0]), 4), "route_scan": round(scan_ms, 4),
@@ -333,9 +396,10 @@ def host_tier_bench(args):
     n_docs = blk.numel() - 1
     blk_d = blk.to(dev)
     tiles = msa.msa_route_tiles(n_blk)
-    krt = torch.empty((L, tiles * 16, 8, 128), dtype=torch.bfloat16, device=dev)
+    krt, contiguous = route_key_memory((L, tiles * 16, 8, 128), torch.bfloat16)
+    krn, _ = route_key_memory((L, tiles * 16, 8), torch.float32)
     for l, rows in di.prepooled_route_rows():
-        msa.msa_pack_route_keys(rows.view(1, n_blk, 8, 128), n_blk, krt[l:l + 1])
+        msa.msa_pack_route_keys(rows.view(1, n_blk, 8, 128), n_blk, krt[l:l + 1], krn[l:l + 1])
     blk_doc = torch.empty(tiles * 16, dtype=torch.int32, device=dev)
     msa.msa_block_doc_map(blk_d, n_blk, blk_doc)
     kh, vh = di.prepooled_content_host()
@@ -372,7 +436,7 @@ def host_tier_bench(args):
     def step(overlap=True):
         for g in range(G):
             l0, l1 = bounds[g], bounds[g + 1]
-            msa.msa_route_scores(qr[l0:l1], krt[l0:l1], n_blk, blk_doc, n_docs, dsc[l0:l1])
+            msa.msa_route_scores(qr[l0:l1], krt[l0:l1], n_blk, blk_doc, n_docs, dsc[l0:l1], krbar_norm=krn[l0:l1])
             s = side if overlap else main
             if overlap:
                 evs[g].record(main)
@@ -391,9 +455,7 @@ def host_tier_bench(args):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / n * 1e3
 
-    for _ in range(args.warmup):
-        step(True)
-        step(False)
+    warm_up(lambda: (step(True), step(False)), args)
     ms_overlap = timed(lambda: step(True), args.steps)
     ms_serial = timed(lambda: step(False), args.steps)
     # the gather alone, from host DRAM and (for scale) from an HBM copy of the selected rows' source
@@ -410,7 +472,7 @@ def host_tier_bench(args):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "10M-token memory, routing keys in HBM (5.76 GB), content K-bar/V-bar in pinned "
                                "host DRAM (11.5 GB), %d queries x 64 tokens, top-16, local 1,024" % B,
-                   "layer_groups": G},
+                   "layer_groups": G, "route_key_alloc": "one contiguous device allocation" if contiguous else "caching allocator"},
         "ms_serial_one_stream": round(ms_serial, 4),
         "overlap_saving_ms": round(ms_serial - ms_overlap, 4),
         "host_gather_ms_18_layers": round(ms_gather_host, 4),
@@ -445,9 +507,10 @@ def interleaved_bench(args):
     n_docs = blk.numel() - 1
     blk_d = blk.to(dev)
     tiles = msa.msa_route_tiles(n_blk)
-    krt = torch.empty((L, tiles * 16, 8, 128), dtype=torch.bfloat16, device=dev)
+    krt, contiguous = route_key_memory((L, tiles * 16, 8, 128), torch.bfloat16)
+    krn, _ = route_key_memory((L, tiles * 16, 8), torch.float32)
     for l, rows in di.prepooled_route_rows():
-        msa.msa_pack_route_keys(rows.view(1, n_blk, 8, 128), n_blk, krt[l:l + 1])
+        msa.msa_pack_route_keys(rows.view(1, n_blk, 8, 128), n_blk, krt[l:l + 1], krn[l:l + 1])
     blk_doc = torch.empty(tiles * 16, dtype=torch.int32, device=dev)
     msa.msa_block_doc_map(blk_d, n_blk, blk_doc)
     qr = di.qr()
@@ -466,16 +529,14 @@ def interleaved_bench(args):
         for r in range(n_r):
             if evs is not None:
                 evs[2 * r].record()
-            msa.msa_route_scores(qr_rounds[r], krt, n_blk, blk_doc, n_docs, dsc, accumulate=r > 0)
+            msa.msa_route_scores(qr_rounds[r], krt, n_blk, blk_doc, n_docs, dsc, accumulate=r > 0, krbar_norm=krn)
             if evs is not None:
                 evs[2 * r + 1].record()
             msa.msa_topk_docs(dsc, k, ids, tsc, ws)
         if evs is not None:
             evs[2 * n_r].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_r + 1)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -506,9 +567,10 @@ def interleaved_bench(args):
         "ms_per_step": round(wall * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.description or "interleaved re-routing", "layers": L, "queries": B,
-                   "rounds_query_tokens": list(cfg.T_rounds), "blocks_per_layer": n_blk, "docs": n_docs, "top_k": k},
+                   "rounds_query_tokens": list(cfg.T_rounds), "blocks_per_layer": n_blk, "docs": n_docs, "top_k": k,
+                   "route_key_alloc": "one contiguous device allocation" if contiguous else "caching allocator", "scan_key_norms": "read"},
         "rounds": rounds,
-        "roofline": {"bound": "mfma", "kernel": "route_mfma_kernel<4, false> (msa_route_scores, round %d)" % (big + 1),
+        "roofline": {"bound": "mfma", "kernel": "route_mfma_kernel<4, false, true> (msa_route_scores, round %d)" % (big + 1),
                      "achieved": rounds[big]["scan_TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": rounds[big]["frac_of_mfma_peak"], "traffic": None},
         "needles_of_query_0_selected": needle_ok,
@@ -537,9 +599,7 @@ def prefill_bench(args):
     def step():
         msa.msa_sparse_prefill(q, ck, cv, cl, lk, lv, ll, scale, out)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
@@ -629,9 +689,7 @@ def encode_bench(args):
     def step():
         msa.msa_encode_blocks(x, wk, wv, wr, wn, eps, theta, tok_d, blk_d, n_blk, kbar, vbar, krt, krn)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()

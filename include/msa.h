@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 #define MSA_HEADS 8          /* KV heads per routed layer                        [P5 方法拆解] */
 #define MSA_HEAD_DIM 128     /* head dimension                                   [P5 方法拆解] */
 #define MSA_BLOCK_TOKENS 64  /* pooling_kernel_size: tokens per compressed block [P2 3.3.2] */
@@ -101,8 +101,8 @@ int msa_block_offsets_host(const int64_t* doc_tok_off_host, int32_t n_docs,
  *
  * so each 1 KiB of a tile is one matrix-core operand fragment for 16 blocks.
  * Sizes per layer: msa_route_tiles(n_blk) * 16384 bf16 and * 128 floats.  The norms
- * are an optional output of the pooling/packing calls (the routing scan recomputes
- * them from the keys it streams, so it reads nothing else). */
+ * are an optional output of the pooling/packing calls and an optional input of the
+ * routing scan (which otherwise recomputes them from the keys it streams). */
 int64_t msa_route_tiles(int64_t n_blk);
 
 /* ------------------------------------------------------------- A1: block pooling
@@ -153,6 +153,13 @@ int msa_block_doc_map(const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk,
  *
  *   qr           [n_layers][B][T][8][128] bf16
  *   krbar_route  route-key layout of n_blk blocks per layer
+ *   krbar_norm   the keys' norms as msa_pool_blocks / msa_pack_route_keys wrote them, or
+ *                NULL.  When given, the matrix-core scan (T >= 16) reads them (32 more bytes
+ *                per block and layer) instead of recomputing them from the keys: worth it
+ *                when B * ceil(T / 64) > 1 makes the scan bound by the matrix cores, not
+ *                for one query chunk, which is bound by HBM.  Both are norms of the same
+ *                bf16 keys; results with and without may differ in the last fp32 bits,
+ *                so calls whose scores are max-merged (accumulate) should agree on it.
  *   blk_doc      block -> document map (msa_block_doc_map) of the same memory
  *   doc_scores   [n_layers][B][n_docs] fp32, output (accumulate = 0) or in/out
  *                (accumulate = 1: the result is max(previous value, new scores),
@@ -162,7 +169,7 @@ int msa_block_doc_map(const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk,
  * Queries with T >= 16 use bf16 matrix cores (fp32 accumulate); shorter ones use
  * vector dot products.  Errors: NULL pointers, n_layers/B/T/n_docs < 1, n_blk < 0. */
 int msa_route_scores(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
-                     const uint16_t* krbar_route, int64_t n_blk,
+                     const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
                      const int32_t* blk_doc, int32_t n_docs, int32_t accumulate,
                      float* doc_scores, void* stream);
 
@@ -186,7 +193,7 @@ int msa_topk_docs(int32_t n_layers, int32_t B, const float* doc_scores, int32_t 
  * NULL; if given it receives a copy of them). */
 size_t msa_route_topk_workspace_size(int32_t n_layers, int32_t B, int32_t n_docs, int32_t k);
 int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
-                   const uint16_t* krbar_route, int64_t n_blk,
+                   const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
                    const int32_t* blk_doc, int32_t n_docs, int32_t k,
                    int32_t* topk_ids, float* topk_scores, float* doc_scores,
                    void* workspace, size_t workspace_bytes, void* stream);

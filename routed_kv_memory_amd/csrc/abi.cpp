@@ -178,12 +178,12 @@ static int check_route_args(const char* fn, int32_t n_layers, const uint16_t* qr
 }
 
 MSA_API int msa_route_scores(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T, const uint16_t* krbar_route,
-                             int64_t n_blk, const int32_t* blk_doc, int32_t n_docs, int32_t accumulate,
+                             const float* krbar_norm, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs, int32_t accumulate,
                              float* doc_scores, void* stream) {
   int st = check_route_args("msa_route_scores", n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs);
   if (st) return st;
   if (!doc_scores) return fail(MSA_ERR_NULL, "msa_route_scores: null pointer");
-  return hip_status(msa::launch_route_scores(n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs,
+  return hip_status(msa::launch_route_scores(n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs,
                                              accumulate ? 1 : 0, doc_scores, as_stream(stream)),
                     "msa_route_scores");
 }
@@ -220,7 +220,7 @@ MSA_API size_t msa_route_topk_workspace_size(int32_t n_layers, int32_t B, int32_
 }
 
 MSA_API int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T, const uint16_t* krbar_route,
-                           int64_t n_blk, const int32_t* blk_doc, int32_t n_docs, int32_t k, int32_t* topk_ids,
+                           const float* krbar_norm, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs, int32_t k, int32_t* topk_ids,
                            float* topk_scores, float* doc_scores, void* workspace, size_t workspace_bytes,
                            void* stream) {
   int st = check_route_args("msa_route_topk", n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs);
@@ -236,7 +236,8 @@ MSA_API int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int3
   float* scores = doc_scores ? doc_scores : reinterpret_cast<float*>(ws);
   char* rest = ws + align256((size_t)n_layers * B * n_docs * sizeof(float));
   hipStream_t s = as_stream(stream);
-  hipError_t e = msa::launch_route_scores(n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs, 0, scores, s);
+  hipError_t e =
+      msa::launch_route_scores(n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs, 0, scores, s);
   if (e != hipSuccess) return hip_status(e, "msa_route_topk (scores)");
   e = msa::launch_topk((int64_t)n_layers * B, scores, n_docs, k, topk_ids, topk_scores, rest, s);
   if (e != hipSuccess) return hip_status(e, "msa_route_topk (top-k)");

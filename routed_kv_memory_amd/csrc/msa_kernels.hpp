@@ -28,7 +28,7 @@ hipError_t launch_pack(int32_t L, const uint16_t* rows, int64_t n_blk, uint16_t*
 // route.hip
 hipError_t launch_blk_doc(const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk, int32_t* blk_doc, hipStream_t s);
 hipError_t launch_route_scores(int32_t L, const uint16_t* qr, int32_t B, int32_t T, const uint16_t* krt,
-                               int64_t n_blk, const int32_t* blk_doc, int32_t n_docs,
+                               const float* knorm, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs,
                                int32_t accumulate, float* doc_scores, hipStream_t s);
 
 // topk.hip

@@ -94,8 +94,11 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 // v_mfma_f32_16x16x32_bf16, so lane l ends up owning block (l & 15) and tokens
 // 4*(l >> 4) + r of each 16-token group.  Per head four more MFMAs of the key
 // fragments with themselves give K K^T, whose diagonal is the blocks' squared
-// norms; the fp32 accumulators are scaled by 1/(|q| |k|) and added into the
-// lane's running head sum, all in registers.
+// norms (when the caller passes the keys' norms the scan reads those instead and
+// skips these products: worth it when several query chunks make the scan bound by
+// the matrix cores); the fp32 accumulators are scaled by 1/(|q| |k|) and added
+// into the lane's running head sum, all in registers.  The key addresses are wave-uniform (scalar
+// registers) plus each lane's 16 bytes, so the ring's bookkeeping is scalar work.
 // After the 8th head the lane takes the max over its tokens, a cross-lane max
 // completes it over the 64 tokens, and the block maxima are folded into
 // per-document maxima: a segmented scan over the 16 blocks, with each document's
@@ -131,14 +134,24 @@ __device__ __forceinline__ void emit_doc(uint32_t* __restrict__ codes, int32_t d
   else codes[doc] = ordered_code(v);
 }
 
+// A wave-uniform 64-bit value moved to scalar registers (the compiler cannot always prove it).
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // STREAM: the keys are read once (one query chunk per range), so nontemporal loads
 // keep them from displacing other lines; with several query chunks the workgroups
 // sharing a range re-read each tile, and ordinary loads let L2 serve the repeats.
-template <int NT, bool STREAM>
+// NORMS: the key norms come from knorm ([layer][tile][head][16] fp32) instead of the
+// K K^T products.
+template <int NT, bool STREAM, bool NORMS>
 __global__ void __launch_bounds__(kScanWG)
 route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t n_tc,
                   const uint4* __restrict__ krt, int64_t tiles, const int32_t* __restrict__ blk_doc,
-                  int32_t n_docs, int32_t L, int32_t R, int32_t exclusive, uint32_t* __restrict__ codes) {
+                  int32_t n_docs, int32_t L, int32_t R, int32_t exclusive, uint32_t* __restrict__ codes,
+                  const float* __restrict__ knorm) {
   __shared__ u32x4 QS[kHeads][4][NT][64];      // query fragments [head][k step][token group][lane]
   __shared__ float RQ[kHeads][kTokChunk];        // 1/max(|q|, eps) per head and token of the chunk
 
@@ -165,13 +178,14 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
   const int64_t it_end = W * (r + 1) / R;
   if (it_begin >= it_end) return;                // uniform across the workgroup
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar registers
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int j = lane & 15;
   const float ninf = -__builtin_huge_valf();
 
   // accumulator row (nt, r) of this lane is token t_base + 16 nt + 4 g + r
+  const bool full_chunk = t_base + NT * 16 <= T;   // uniform: every row is a valid token
   uint32_t tmask = 0;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -215,25 +229,34 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
     const int64_t n_tw = w0 < w1 ? (w1 - w0 + tstep - 1) / tstep : 0;   // tiles of this wave
     if (n_tw > 0) {
       uint32_t* lcodes = codes + ((int64_t)layer * B + b) * n_docs;
-      const int64_t n_units = n_tw * kHeads;        // key slices of the wave's tiles
-      const uint4* src = krt + w0 * kTileU4 + lane;
+      const int64_t n_units = uniform64(n_tw * kHeads);   // key slices of the wave's tiles
+      // the slice address is wave-uniform; each lane adds its own 16 bytes.  NORMS: the
+      // norms of heads 4q .. 4q + 3 of a tile (64 floats, lane l: head 4q + (l >> 4), block
+      // l & 15) are loaded with the tile's slice 4q into hn[q], which the next load into it
+      // (four slices later) replaces only after those heads are done.
+      const u32x4* src = reinterpret_cast<const u32x4*>(krt + w0 * kTileU4);
+      const float* nsrc = NORMS ? knorm + w0 * (kHeads * kTile) : nullptr;   // this slice's 16 norms
       int64_t unext = 0;
       u32x4 kb[kRing][4];
+      float hn[2];
       // Loads are unconditional (past the run's end the last slice is fetched again)
       // so that every wait is an exact count.
-      auto issue = [&](u32x4 (&kbuf)[4]) {
+      auto issue = [&](u32x4 (&kbuf)[4], int slice) {   // slice: head of the issued slice (static)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          kbuf[s] = STREAM ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + s * 64))
-                           : *reinterpret_cast<const u32x4*>(src + s * 64);
+          kbuf[s] = STREAM ? __builtin_nontemporal_load(src + lane + s * 64) : src[lane + s * 64];
+        if (NORMS && (slice & 3) == 0)   // from the tile's start: in bounds when the ring is clamped
+          hn[slice >> 2] = nsrc[(slice - (int)(unext & (kHeads - 1))) * kTile + lane];
         if (unext + 1 < n_units) {
           ++unext;
-          src += (unext & (kHeads - 1)) == 0 ? (tstep - 1) * kTileU4 + kHeadU4 : kHeadU4;
+          const int64_t step = (unext & (kHeads - 1)) == 0 ? (tstep - 1) * kTileU4 + kHeadU4 : kHeadU4;
+          src += step;
+          if (NORMS) nsrc += step / (kHeadU4 / kTile);   // 16 norms per 256-uint4 slice
         }
       };
 #pragma unroll
       for (int x = 0; x < kAhead; ++x) {
-        issue(kb[x]);
+        issue(kb[x], x);
         __builtin_amdgcn_sched_barrier(0);   // keep the ring's issue order (exact wait counts)
       }
 
@@ -250,7 +273,7 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
         for (int h = 0; h < kHeads; ++h) {
           // keeps each head's query-fragment reads from being hoisted into earlier heads
           __builtin_amdgcn_sched_barrier(0);
-          issue(kb[(h + kAhead) % kRing]);
+          issue(kb[(h + kAhead) % kRing], (h + kAhead) % kHeads);
           if (h == 0) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) tot[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -269,18 +292,25 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
             for (int nt = 0; nt < NT; ++nt)
               acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, QS[h][s][nt][lane]), kf,
                                                                 acc[nt], 0, 0, 0);
-            kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, kf, kk, 0, 0, 0);
+            if (!NORMS) kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, kf, kk, 0, 0, 0);
           }
-          // |k_j|^2 is the diagonal entry (j, j): row j = 4 g + r sits in lane group
-          // g = j >> 2, register r = j & 3; the sum over the 4 lane groups hands it
-          // to every lane of block j.
-          const int jr = j & 3;
-          const float k01 = (jr & 1) ? kk[1] : kk[0];
-          const float k23 = (jr & 1) ? kk[3] : kk[2];
-          float ssk = (jr & 2) ? k23 : k01;
-          ssk = rows4_sum(g == (j >> 2) ? ssk : 0.f);
-          // 1/max(|k|, eps) = rsq(max(|k|^2, eps^2))
-          const float rk = __builtin_amdgcn_rsqf(fmaxf(ssk, kNormEps * kNormEps));   // block j, head h
+          float rk;   // 1/max(|k|, eps) of block j, head h
+          if (NORMS) {
+            // head h, block j: lane 16 (h & 3) + j of hn[h >> 2]
+            const float nh = __int_as_float(
+                __builtin_amdgcn_ds_bpermute((16 * (h & 3) + j) * 4, __float_as_int(hn[h >> 2])));
+            rk = __builtin_amdgcn_rcpf(fmaxf(nh, kNormEps));
+          } else {
+            // |k_j|^2 is the diagonal entry (j, j): row j = 4 g + r sits in lane group
+            // g = j >> 2, register r = j & 3; the sum over the 4 lane groups hands it
+            // to every lane of block j.
+            const int jr = j & 3;
+            const float k01 = (jr & 1) ? kk[1] : kk[0];
+            const float k23 = (jr & 1) ? kk[3] : kk[2];
+            float ssk = (jr & 2) ? k23 : k01;
+            ssk = rows4_sum(g == (j >> 2) ? ssk : 0.f);
+            rk = __builtin_amdgcn_rsqf(fmaxf(ssk, kNormEps * kNormEps));   // = 1/max(|k|, eps)
+          }
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             const float4 rq = *reinterpret_cast<const float4*>(&RQ[h][nt * 16 + 4 * g]);   // tokens 4 g + r
@@ -293,11 +323,18 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
           if (h == kHeads - 1) {
             // block j's max over the chunk's valid tokens, as a head mean
             float v = ninf;
+            if (full_chunk) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+              for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr)
-                if (tmask & (1u << (nt * 4 + rr))) v = fmaxf(v, tot[nt][rr]);
+                for (int rr = 0; rr < 4; ++rr) v = fmaxf(v, tot[nt][rr]);
+            } else {
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                  if (tmask & (1u << (nt * 4 + rr))) v = fmaxf(v, tot[nt][rr]);
+            }
             v = rows4_max(v) * 0.125f;
 
             // Fold the tile's 16 block maxima into document maxima.  Blocks of a
@@ -477,7 +514,7 @@ hipError_t launch_blk_doc(const int64_t* doc_blk_off, int32_t n_docs, int64_t n_
 }
 
 hipError_t launch_route_scores(int32_t L, const uint16_t* qr, int32_t B, int32_t T, const uint16_t* krt,
-                               int64_t n_blk, const int32_t* blk_doc, int32_t n_docs,
+                               const float* knorm, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs,
                                int32_t accumulate, float* doc_scores, hipStream_t s) {
   const int64_t tiles = route_tiles(n_blk);
   const int64_t n_codes = (int64_t)L * B * n_docs;
@@ -495,16 +532,25 @@ hipError_t launch_route_scores(int32_t L, const uint16_t* qr, int32_t B, int32_t
       const dim3 grid((unsigned)(R * C));
       const uint4* kt = reinterpret_cast<const uint4*>(krt);
       const int excl = (n_tc == 1 && !accumulate) ? 1 : 0;
-#define MSA_ROUTE_LAUNCH(NTV, ST)                                                                          \
-  hipLaunchKernelGGL((route_mfma_kernel<NTV, ST>), grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, tiles, blk_doc, \
-                     n_docs, L, R, excl, codes)
+#define MSA_ROUTE_LAUNCH(NTV, ST, NM)                                                                       \
+  hipLaunchKernelGGL((route_mfma_kernel<NTV, ST, NM>), grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, tiles,   \
+                     blk_doc, n_docs, L, R, excl, codes, knorm)
+#define MSA_ROUTE_NT(NTV)                                          \
+  if (stream) {                                                    \
+    if (knorm) MSA_ROUTE_LAUNCH(NTV, true, true);                  \
+    else MSA_ROUTE_LAUNCH(NTV, true, false);                       \
+  } else {                                                         \
+    if (knorm) MSA_ROUTE_LAUNCH(NTV, false, true);                 \
+    else MSA_ROUTE_LAUNCH(NTV, false, false);                      \
+  }
       const bool stream = C == 1;
       switch (NT) {
-        case 1: if (stream) MSA_ROUTE_LAUNCH(1, true); else MSA_ROUTE_LAUNCH(1, false); break;
-        case 2: if (stream) MSA_ROUTE_LAUNCH(2, true); else MSA_ROUTE_LAUNCH(2, false); break;
-        case 3: if (stream) MSA_ROUTE_LAUNCH(3, true); else MSA_ROUTE_LAUNCH(3, false); break;
-        default: if (stream) MSA_ROUTE_LAUNCH(4, true); else MSA_ROUTE_LAUNCH(4, false); break;
+        case 1: MSA_ROUTE_NT(1); break;
+        case 2: MSA_ROUTE_NT(2); break;
+        case 3: MSA_ROUTE_NT(3); break;
+        default: MSA_ROUTE_NT(4); break;
       }
+#undef MSA_ROUTE_NT
 #undef MSA_ROUTE_LAUNCH
     } else {
       const dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)B, (unsigned)L);

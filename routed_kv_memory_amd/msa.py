@@ -37,11 +37,11 @@ _SIGS = {
     "msa_pool_blocks": ([_I32, _P, _P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "msa_pack_route_keys": ([_I32, _P, _I64, _P, _P, _P], ctypes.c_int),
     "msa_block_doc_map": ([_P, _I32, _I64, _P, _P], ctypes.c_int),
-    "msa_route_scores": ([_I32, _P, _I32, _I32, _P, _I64, _P, _I32, _I32, _P, _P], ctypes.c_int),
+    "msa_route_scores": ([_I32, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I32, _P, _P], ctypes.c_int),
     "msa_topk_docs_workspace_size": ([_I32, _I32, _I32, _I32], _SZ),
     "msa_topk_docs": ([_I32, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "msa_route_topk_workspace_size": ([_I32, _I32, _I32, _I32], _SZ),
-    "msa_route_topk": ([_I32, _P, _I32, _I32, _P, _I64, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "msa_route_topk": ([_I32, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "msa_gather_ctx": ([_I32, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _I64, _I32, _P, _P, _P, _P], ctypes.c_int),
     "msa_sparse_decode_workspace_size": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_decode": ([_I32, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _F32, _P, _P, _SZ, _P],
@@ -169,11 +169,22 @@ def msa_block_doc_map(doc_blk_off, n_blk, blk_doc, stream=None):
         _ptr(doc_blk_off, _I64T, "doc_blk_off"), n_docs, n_blk, _ptr(blk_doc, _I32T, "blk_doc"), _stream(stream)))
 
 
-def msa_route_scores(qr, krbar_route, n_blk, blk_doc, n_docs, doc_scores, accumulate=False, stream=None):
+def _norms(krbar_norm, n_layers, n_blk):
+    """The optional key norms of the scan: None, or at least [n_layers][tiles][8][16] fp32."""
+    if krbar_norm is None:
+        return None
+    need = n_layers * msa_route_tiles(n_blk) * 128
+    if krbar_norm.numel() < need:
+        raise ValueError("krbar_norm has %d elements, the scan needs %d" % (krbar_norm.numel(), need))
+    return _ptr(krbar_norm, _F32T, "krbar_norm")
+
+
+def msa_route_scores(qr, krbar_route, n_blk, blk_doc, n_docs, doc_scores, accumulate=False, stream=None,
+                     krbar_norm=None):
     L, B, T = qr.shape[0], qr.shape[1], qr.shape[2]
     _check("msa_route_scores", lib().msa_route_scores(
         L, _ptr(qr, _BF16, "qr"), B, T, _ptr(krbar_route, _BF16, "krbar_route"),
-        n_blk, _ptr(blk_doc, _I32T, "blk_doc"), n_docs,
+        _norms(krbar_norm, L, n_blk), n_blk, _ptr(blk_doc, _I32T, "blk_doc"), n_docs,
         1 if accumulate else 0, _ptr(doc_scores, _F32T, "doc_scores"), _stream(stream)))
 
 
@@ -194,11 +205,11 @@ def msa_route_topk_workspace_size(n_layers, B, n_docs, k) -> int:
 
 
 def msa_route_topk(qr, krbar_route, n_blk, blk_doc, n_docs, k, topk_ids, topk_scores, workspace, doc_scores=None,
-                   stream=None):
+                   stream=None, krbar_norm=None):
     L, B, T = qr.shape[0], qr.shape[1], qr.shape[2]
     _check("msa_route_topk", lib().msa_route_topk(
         L, _ptr(qr, _BF16, "qr"), B, T, _ptr(krbar_route, _BF16, "krbar_route"),
-        n_blk, _ptr(blk_doc, _I32T, "blk_doc"), n_docs, k,
+        _norms(krbar_norm, L, n_blk), n_blk, _ptr(blk_doc, _I32T, "blk_doc"), n_docs, k,
         _ptr(topk_ids, _I32T, "topk_ids"), _ptr(topk_scores, _F32T, "topk_scores", allow_none=True),
         _ptr(doc_scores, _F32T, "doc_scores", allow_none=True), _ptr(workspace, _ANY, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -56,7 +56,9 @@ def doc_map(blk_off_d: torch.Tensor, n_blk: int) -> torch.Tensor:
     return m
 
 
-def route(qr, krt, krn, n_blk, blk_off_d, k, dev="cuda", blk_doc=None):
+def route(qr, krt, krn, n_blk, blk_off_d, k, dev="cuda", blk_doc=None, norms=None):
+    """Scores + top-k through msa_route_topk.  norms: pass the key norms to the scan (True), let
+    it recompute them (False), or None: pass them when the scan has more than one query chunk."""
     L, B = qr.shape[0], qr.shape[1]
     n_docs = blk_off_d.numel() - 1
     if blk_doc is None:
@@ -65,7 +67,10 @@ def route(qr, krt, krn, n_blk, blk_off_d, k, dev="cuda", blk_doc=None):
     ids = torch.empty((L, B, k), dtype=torch.int32, device=dev)
     sc = torch.empty((L, B, k), dtype=torch.float32, device=dev)
     dsc = torch.empty((L, B, n_docs), dtype=torch.float32, device=dev)
-    msa.msa_route_topk(qr, krt, n_blk, blk_doc, n_docs, k, ids, sc, ws, doc_scores=dsc)
+    if norms is None:
+        norms = B * ((qr.shape[2] + 63) // 64) > 1
+    msa.msa_route_topk(qr, krt, n_blk, blk_doc, n_docs, k, ids, sc, ws, doc_scores=dsc,
+                       krbar_norm=krn if norms else None)
     return ids, sc, dsc
 
 

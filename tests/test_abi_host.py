@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(msa):
     L = ctypes.CDLL(LIB)
     missing = [s for s in syms if not hasattr(L, s)]
     assert not missing, missing
-    assert msa.msa_abi_version() == 1
+    assert msa.msa_abi_version() == 2
 
 
 def test_only_msa_symbols_are_exported():
@@ -76,12 +76,12 @@ def test_invalid_arguments_are_rejected_on_the_host(msa):
     lib = msa.lib()
     # null pointers
     assert lib.msa_pool_blocks(1, None, fake, fake, 10, fake, fake, 1, 1, fake, fake, fake, fake, None) == 1
-    assert lib.msa_route_scores(1, None, 1, 8, fake, 16, fake, 1, 0, fake, None) == 1
+    assert lib.msa_route_scores(1, None, 1, 8, fake, None, 16, fake, 1, 0, fake, None) == 1
     assert lib.msa_block_doc_map(None, 4, 16, fake, None) == 1
     # shapes
-    assert lib.msa_route_scores(0, fake, 1, 8, fake, 16, fake, 1, 0, fake, None) == 2
-    assert lib.msa_route_scores(1, fake, 1, 0, fake, 16, fake, 1, 0, fake, None) == 2
-    assert lib.msa_route_topk(1, fake, 1, 8, fake, 16, fake, 4, 5, fake, None, None, fake, 1 << 20, None) == 2
+    assert lib.msa_route_scores(0, fake, 1, 8, fake, None, 16, fake, 1, 0, fake, None) == 2
+    assert lib.msa_route_scores(1, fake, 1, 0, fake, fake, 16, fake, 1, 0, fake, None) == 2
+    assert lib.msa_route_topk(1, fake, 1, 8, fake, None, 16, fake, 4, 5, fake, None, None, fake, 1 << 20, None) == 2
     assert lib.msa_topk_docs(1, 1, fake, 10, 11, fake, None, fake, 1 << 20, None) == 2       # k > n_docs
     assert lib.msa_topk_docs(1, 1, fake, 1000, 300, fake, None, fake, 1 << 20, None) == 3    # k > MAX_TOPK
     assert lib.msa_gather_ctx(1, 1, fake, 4, fake, 10, 8, fake, fake, 100, 31, fake, fake, fake, None) == 2
@@ -110,7 +110,7 @@ def test_invalid_arguments_are_rejected_on_the_host(msa):
                                  fake, fake, None, None) == 2
     # workspace too small
     need = lib.msa_route_topk_workspace_size(2, 1, 100000, 16)
-    assert lib.msa_route_topk(2, fake, 1, 8, fake, 1000, fake, 100000, 16, fake, None, None, fake, need - 1,
+    assert lib.msa_route_topk(2, fake, 1, 8, fake, None, 1000, fake, 100000, 16, fake, None, None, fake, need - 1,
                               None) == 4
     need = lib.msa_sparse_decode_workspace_size(2, 3, 32, 100, 50)
     assert lib.msa_sparse_decode(2, 3, 32, fake, fake, fake, fake, 100, fake, fake, fake, 50, ctypes.c_float(0.1),

@@ -93,8 +93,10 @@ class Memory:
         L, B = qr.shape[0], qr.shape[1]
         if doc_scores is None:
             doc_scores = torch.empty((L, B, self.n_docs), dtype=torch.float32, device=DEV)
+        # key norms passed when the scan has several query chunks (as bench.py runs it)
+        norms = self.krn if B * ((qr.shape[2] + 63) // 64) > 1 else None
         msa.msa_route_scores(qr, self.krt, self.n_blk, self.blk_doc, self.n_docs, doc_scores,
-                             accumulate=accumulate)
+                             accumulate=accumulate, krbar_norm=norms)
         ids = torch.empty((L, B, k), dtype=torch.int32, device=DEV)
         sc = torch.empty((L, B, k), dtype=torch.float32, device=DEV)
         ws = torch.empty(max(msa.msa_topk_docs_workspace_size(L, B, self.n_docs, k), 256), dtype=torch.uint8,

@@ -94,9 +94,10 @@ def _memory(rng, L, lens_blocks):
     return off, n_blk, rows
 
 
+@pytest.mark.parametrize("norms", [False, True])
 @pytest.mark.parametrize("T,B", [(1, 1), (5, 2), (15, 1), (16, 1), (17, 2), (40, 1), (64, 1), (65, 2), (130, 1)])
-def test_route_scores_and_topk_shapes(T, B):
-    print("case: route T=%d B=%d" % (T, B), flush=True)
+def test_route_scores_and_topk_shapes(T, B, norms):
+    print("case: route T=%d B=%d norms=%d" % (T, B, norms), flush=True)
     rng = np.random.default_rng(1000 + T * 7 + B)
     L = 2
     lens = rng.integers(1, 9, 45)
@@ -109,7 +110,7 @@ def test_route_scores_and_topk_shapes(T, B):
     krt, krn = pack_rows(to_dev_bf16(rows), n_blk)
     blk_d = torch.from_numpy(off).to(DEV)
     k = 7
-    ids, sc, dsc = route(to_dev_bf16(qr), krt, krn, n_blk, blk_d, k)
+    ids, sc, dsc = route(to_dev_bf16(qr), krt, krn, n_blk, blk_d, k, norms=norms)
     torch.cuda.synchronize()
     assert np.array_equal(untile_keys(krt, n_blk), rows)
     assert np.allclose(untile_norms(krn, n_blk), O.head_norms(rows), rtol=1e-6, atol=0)
@@ -125,9 +126,11 @@ def test_route_scores_and_topk_shapes(T, B):
     assert abs(dsc_h[0, 0, 5] - 1.0) < SCORE_TOL and abs(dsc_h[1, B - 1, 30] - 1.0) < SCORE_TOL
 
 
-def test_route_accumulate_equals_full_query():
-    """Re-routing a grown query by max-merging the appended rows' scores is exact."""
-    print("case: route accumulate", flush=True)
+@pytest.mark.parametrize("norms", [False, True])
+def test_route_accumulate_equals_full_query(norms):
+    """Re-routing a grown query by max-merging the appended rows' scores is exact (every call
+    either reads the key norms or recomputes them)."""
+    print("case: route accumulate norms=%d" % norms, flush=True)
     rng = np.random.default_rng(7)
     L, B = 2, 2
     off, n_blk, rows = _memory(rng, L, rng.integers(1, 20, 60))
@@ -136,12 +139,13 @@ def test_route_accumulate_equals_full_query():
     qr = rand_bf16(rng, (L, B, 64 + 128, 8, 128))
     n_docs = len(off) - 1
     m = doc_map(blk_d, n_blk)
+    nrm = krn if norms else None
     full = torch.empty((L, B, n_docs), dtype=torch.float32, device=DEV)
-    msa.msa_route_scores(to_dev_bf16(qr), krt, n_blk, m, n_docs, full)
+    msa.msa_route_scores(to_dev_bf16(qr), krt, n_blk, m, n_docs, full, krbar_norm=nrm)
     inc = torch.empty_like(full)
-    msa.msa_route_scores(to_dev_bf16(qr[:, :, :64]), krt, n_blk, m, n_docs, inc)
+    msa.msa_route_scores(to_dev_bf16(qr[:, :, :64]), krt, n_blk, m, n_docs, inc, krbar_norm=nrm)
     first = inc.clone()
-    msa.msa_route_scores(to_dev_bf16(qr[:, :, 64:]), krt, n_blk, m, n_docs, inc, accumulate=True)
+    msa.msa_route_scores(to_dev_bf16(qr[:, :, 64:]), krt, n_blk, m, n_docs, inc, accumulate=True, krbar_norm=nrm)
     torch.cuda.synchronize()
     assert torch.equal(inc, full)
     assert bool((inc >= first).all())
