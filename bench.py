@@ -35,7 +35,7 @@ POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 # profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
 # sources' digest differs, the figure is stale and bench.py reports null.
 SCAN_TRAFFIC_BYTES = 57.693e9
-SCAN_TRAFFIC_SOURCE_DIGEST = "4494e72ddab2cdff98e1c1fbb143dabe59a979bec1dbe7a81edc89b5ae597860"
+SCAN_TRAFFIC_SOURCE_DIGEST = "c72ad31273b5026d9501aac630d7decd4de1ad73b82da9ba19c89321cad240be"
 
 
 # HBM traffic of one encode launch (18 layers, 1M-token document set), FETCH_SIZE + WRITE_SIZE

@@ -477,29 +477,45 @@ route_valu_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, const u
   flush_doc_max(m, doc, kTile, n_docs, codes + ((int64_t)layer * B + b) * n_docs);
 }
 
-int choose_ranges(int C, int cus) {
+constexpr int64_t kMaxRangeTiles = 1024;   // per range when several query chunks share it
+
+int choose_ranges(int C, int cus, int64_t W) {
   // R ranges per query chunk; the persistent grid of R*C workgroups (one per CU at a
   // time) should fill whole waves of the device: pick R in [ceil(cus/C), 4*ceil(cus/C)]
   // with the best filled fraction.  When several query chunks share each range, a
   // multiple of 8 wins ties, so that each range's workgroups sit on one XCD (one L2);
   // otherwise the smallest R wins.
-  if (C >= cus) return 1;
-  const int r0 = (cus + C - 1) / C;
-  int best = r0;
-  double best_eff = 0.0;
-  bool best_x8 = false;
-  for (int R = r0; R <= 4 * r0; ++R) {
-    const long total = (long)R * C;
-    const long waves = (total + cus - 1) / cus;
-    const double eff = (double)total / (double)(waves * cus);
-    const bool x8 = C > 1 && (R & 7) == 0;
-    if (eff > best_eff + 1e-9 || (eff > best_eff - 1e-9 && x8 && !best_x8)) {
-      best_eff = eff;
-      best = R;
-      best_x8 = x8;
+  int best = 1;
+  if (C < cus) {
+    const int r0 = (cus + C - 1) / C;
+    best = r0;
+    double best_eff = 0.0;
+    bool best_x8 = false;
+    for (int R = r0; R <= 4 * r0; ++R) {
+      const long total = (long)R * C;
+      const long waves = (total + cus - 1) / cus;
+      const double eff = (double)total / (double)(waves * cus);
+      const bool x8 = C > 1 && (R & 7) == 0;
+      if (eff > best_eff + 1e-9 || (eff > best_eff - 1e-9 && x8 && !best_x8)) {
+        best_eff = eff;
+        best = R;
+        best_x8 = x8;
+      }
     }
   }
-  return best;
+  if (C == 1) return best;
+  // Shared ranges are kept short: the workgroups reading one range drift apart over a long
+  // run until the tiles one of them fetched are gone from L2 before the others read them.
+  // Ranges of at most kMaxRangeTiles tiles (32 MiB) keep the repeats in L2; R stays a
+  // multiple of 8 and, where one is near, R*C a whole number of waves.
+  // (The grid, R*C workgroups, stays below 2^31.)
+  const int64_t rcap = (int64_t)0x7FFFFFFF / C;
+  int64_t rmin = (W + kMaxRangeTiles - 1) / kMaxRangeTiles;
+  if (rmin <= best || best >= rcap) return best;
+  rmin = (rmin + 7) / 8 * 8;
+  for (int64_t R = rmin; R <= rmin + 8 * 64 && R <= rcap; R += 8)
+    if ((R * C) % cus == 0) return (int)R;
+  return (int)(rmin < rcap ? rmin : rcap);
 }
 
 }  // namespace
@@ -527,7 +543,7 @@ hipError_t launch_route_scores(int32_t L, const uint16_t* qr, int32_t B, int32_t
     if (T >= 16) {
       const int n_tc = (T + kTokChunk - 1) / kTokChunk;
       const int C = B * n_tc;
-      const int R = choose_ranges(C, cus);
+      const int R = choose_ranges(C, cus, (int64_t)L * tiles);
       const int NT = T >= kTokChunk ? 4 : (T + 15) / 16;
       const dim3 grid((unsigned)(R * C));
       const uint4* kt = reinterpret_cast<const uint4*>(krt);
