@@ -34,8 +34,8 @@ POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 # WRITE_SIZE rocprofv3 passes (scaled by a 1 GiB calibration kernel) recorded in
 # profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
 # sources' digest differs, the figure is stale and bench.py reports null.
-SCAN_TRAFFIC_BYTES = 57.693e9
-SCAN_TRAFFIC_SOURCE_DIGEST = "c72ad31273b5026d9501aac630d7decd4de1ad73b82da9ba19c89321cad240be"
+SCAN_TRAFFIC_BYTES = 57.793e9
+SCAN_TRAFFIC_SOURCE_DIGEST = "8f7de23cb54b24ccb86c1241f293b47b95836f9e250071faeb88be5743667f86"
 
 
 # HBM traffic of one encode launch (18 layers, 1M-token document set), FETCH_SIZE + WRITE_SIZE
