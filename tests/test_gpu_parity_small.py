@@ -173,7 +173,7 @@ def test_topk_multi_pass_and_ties():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("n_docs,k", [(5, 5), (64, 64), (2048, 1), (2048, 64), (2049, 64), (2049, 3),
-                                      (4097, 16), (6144, 64), (131072, 16)])
+                                      (4097, 16), (6144, 64), (131072, 16), (256, 256), (1000, 256), (70000, 256)])
 def test_topk_chunk_edges(n_docs, k):
     """Row lengths at and around the selection chunk, k equal to the row length, k at the
     register path's limit; every score equal in one row (order by id alone)."""
