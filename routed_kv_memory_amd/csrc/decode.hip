@@ -7,15 +7,15 @@
 // 架构; xuqi2024.github.io "【MSA】突破100M Token 上下文…", 5.2; xiaohongrsx.github.io
 // "MSA paper reading", 推理全流程).
 //
-// Layout of the work: one workgroup per (128-row split, KV head, layer x query); each of
-// its 4 waves takes 32 of the split's rows for all G query heads of the KV head, so the
+// Layout of the work: one workgroup per (256-row split, KV head, layer x query); each of
+// its 8 waves takes 32 of the split's rows for all G query heads of the KV head, so the
 // heads share every K and V read.  On the matrix cores (v_mfma_f32_16x16x32_bf16) the
 // G heads are the 16-wide column side: S^T = K . Q^T takes the keys as the A operand,
 // loaded from global memory straight into fragment layout (lane 16 g + j: key j, dims
 // 8 g .. 8 g + 7 of each 32-dim step); O^T = V^T . P^T takes V^T from the wave's own
 // row-major V tile in LDS through transposed reads (ds_read_b64_tr_b16), and P as a
 // bf16 high part plus a bf16 residual (~16 significant bits).  Every load of a split is
-// issued at once (one memory latency per split).  The 4 waves' (max, sum, output) are
+// issued at once (one memory latency per split).  The 8 waves' (max, sum, output) are
 // combined in LDS into one partial per split and head; a second kernel merges the
 // splits in one pass.  All accumulation is fp32.
 #include "msa_device.hpp"
@@ -24,8 +24,9 @@
 namespace msa {
 namespace {
 
-constexpr int kRowsPerSplit = 128;        // per workgroup
-constexpr int kWaveRows = 32;             // per wave
+constexpr int kSplitWaves = 8;
+constexpr int kWaveRows = 32;                          // per wave
+constexpr int kRowsPerSplit = kWaveRows * kSplitWaves;  // per workgroup
 constexpr int kVStride = kDim + 8;        // bf16 per staged V row
 
 #ifndef MSA_DECODE_LOAD
@@ -33,15 +34,15 @@ constexpr int kVStride = kDim + 8;        // bf16 per staged V row
 #endif
 
 template <int G>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * kSplitWaves)
 decode_split_kernel(int32_t Hq, const uint16_t* __restrict__ q, const uint16_t* __restrict__ ctx_k,
                     const uint16_t* __restrict__ ctx_v, const int32_t* __restrict__ ctx_len, int32_t max_ctx,
                     const uint16_t* __restrict__ loc_k, const uint16_t* __restrict__ loc_v,
                     const int32_t* __restrict__ loc_len, int32_t max_loc, float scale, int32_t n_splits,
                     float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
   // per wave: its K tile, then its V tile (row-major), then its output columns
-  __shared__ uint16_t v_s[4][kWaveRows * kVStride];
-  __shared__ float c_m[4][G], c_l[4][G];
+  __shared__ uint16_t v_s[kSplitWaves][kWaveRows * kVStride];
+  __shared__ float c_m[kSplitWaves][G], c_l[kSplitWaves][G];
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -169,7 +170,7 @@ decode_split_kernel(int32_t Hq, const uint16_t* __restrict__ q, const uint16_t* 
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl, o[dt], 0, 0, 0);
     }
   }
-  // combine the 4 waves: each wave's output columns go to its own V tile's space (its
+  // combine the waves: each wave's output columns go to its own V tile's space (its
   // reads of it are done: one wave's LDS operations complete in order)
   float* co = reinterpret_cast<float*>(vt);   // [G][kDim]
   if (j < G) {
@@ -183,14 +184,14 @@ decode_split_kernel(int32_t Hq, const uint16_t* __restrict__ q, const uint16_t* 
     }
   }
   __syncthreads();
-  for (int i = tid; i < G * kDim; i += 256) {
+  for (int i = tid; i < G * kDim; i += 64 * kSplitWaves) {
     const int h = i / kDim;
     float M = ninf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, c_m[w][h]);
+    for (int w = 0; w < kSplitWaves; ++w) M = fmaxf(M, c_m[w][h]);
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kSplitWaves; ++w) {
       const float c = __builtin_amdgcn_exp2f(c_m[w][h] - M);   // 0 for an inactive wave
       num += c * reinterpret_cast<const float*>(v_s[w])[i];
       den += c * c_l[w][h];
@@ -269,13 +270,13 @@ hipError_t launch_decode(int32_t L, int32_t B, int32_t Hq, const uint16_t* q, co
   float* ws_acc = ws_ml + ((2 * parts + 63) / 64) * 64;
   const dim3 grid((unsigned)n_splits, kHeads, (unsigned)(L * B));
   switch (G) {
-    case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(256), 0, s, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
+    case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(64 * kSplitWaves), 0, s, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
                                loc_k, loc_v, loc_len, max_loc, scale, n_splits, ws_ml, ws_acc); break;
-    case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(256), 0, s, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
+    case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(64 * kSplitWaves), 0, s, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
                                loc_k, loc_v, loc_len, max_loc, scale, n_splits, ws_ml, ws_acc); break;
-    case 4: hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(256), 0, s, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
+    case 4: hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(64 * kSplitWaves), 0, s, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
                                loc_k, loc_v, loc_len, max_loc, scale, n_splits, ws_ml, ws_acc); break;
-    case 8: hipLaunchKernelGGL(decode_split_kernel<8>, grid, dim3(256), 0, s, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
+    case 8: hipLaunchKernelGGL(decode_split_kernel<8>, grid, dim3(64 * kSplitWaves), 0, s, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
                                loc_k, loc_v, loc_len, max_loc, scale, n_splits, ws_ml, ws_acc); break;
     default: return hipErrorInvalidValue;
   }

@@ -264,13 +264,13 @@ def test_gather_decode_edges(Hq):
 
 @pytest.mark.parametrize("Hq", [8, 64])
 def test_decode_row_count_boundaries(Hq):
-    """Total row counts around the 32-row wave and 128-row split boundaries, with the memory /
-    local seam inside a wave's rows."""
+    """Total row counts around the 32-row wave and the 256-row split boundaries (and 128), with
+    the memory / local seam inside a wave's rows."""
     print("case: decode boundaries Hq=%d" % Hq, flush=True)
     rng = np.random.default_rng(29 + Hq)
-    totals = [1, 31, 32, 33, 127, 128, 129, 255, 256, 257]
+    totals = [1, 31, 32, 33, 127, 128, 129, 255, 256, 257, 511, 512, 513]
     L, B = 1, len(totals)
-    max_ctx, max_loc = 160, 160
+    max_ctx, max_loc = 300, 300
     ck, cv = rand_bf16(rng, (L, B, max_ctx, 8, 128)), rand_bf16(rng, (L, B, max_ctx, 8, 128))
     lk, lv = rand_bf16(rng, (L, B, max_loc, 8, 128)), rand_bf16(rng, (L, B, max_loc, 8, 128))
     q = rand_bf16(rng, (L, B, Hq, 128))
