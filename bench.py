@@ -22,6 +22,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "routing scan GB/s (% HBM peak) + ms/query, 18 layers, 100M-token memory"
+# What each per-workload line reports (the 100M-token line carries the headline metric).
+WORKLOAD_METRICS = {
+    "100m": (METRIC, "GB/s", True),
+    "10m": ("routing scan TFLOP/s (% of bf16 MFMA peak) over whole steps, 18 layers, 10M-token memory, "
+            "32 queries x 64 tokens", "TFLOP/s", True),
+    "1m": ("tokens/s through the whole path (pool, route, top-k, gather, decode), 18 layers, "
+           "1M-token memory", "tokens/s", True),
+    "tiny": ("ms per step of the whole path (pool, route, top-k, gather, decode), tiny workload: 1 layer, "
+             "64 documents", "ms", False),
+}
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0             # dense bf16 matrix-core peak
 SCAN_BYTES_PER_BLOCK_LAYER = 2048         # bf16 Kr-bar row (8 x 128): key norms are computed in-kernel
@@ -285,15 +295,22 @@ def main():
                     "traffic_unit": "GB per launch", "algorithmic_GB_per_launch": round(scan_bytes / 1e9, 3)}
     ctx_rows = int(cl.sum().item())
     dec_rows = ctx_rows + int(ll.sum().item())
+    metric, unit, higher = WORKLOAD_METRICS[cfg.name]
+    if cfg.name == "10m":
+        value = scan_flop * args.steps / wall / 1e12                 # TFLOP/s over whole steps
+    elif cfg.name == "1m":
+        value = L * n_tok * args.steps / wall                       # tokens/s through the path
+    elif cfg.name == "tiny":
+        value = ms_step
     result = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
+        "metric": metric,
+        "value": round(value, 4 if unit == "ms" else 2),
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
+        "higher_is_better": higher,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
@@ -306,7 +323,8 @@ def main():
             "route_key_alloc": "one contiguous device allocation" if contiguous else "caching allocator",
             "scan_key_norms": "read" if scan_norms is not None else "recomputed from the keys",
         },
-        "hbm_frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+        "scan_GBps_over_whole_steps": round(scan_bytes * args.steps / wall / 1e9, 2),
+        "hbm_frac_of_peak": round(scan_bytes * args.steps / wall / 1e9 / HBM_PEAK_GBPS, 4),
         "ms_per_query_18_layers": round(ms_step / B, 4),
         "ms_per_query_per_layer": round(ms_step / B / L, 5),
         "scan_ms": round(scan_ms, 4),
@@ -366,7 +384,7 @@ def main():
         del ck, cv
         result["calibration_copy_bytes"] = calibration_copy(dev)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, n_blk, blk.numpy(), args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(cfg, di, blk.numpy(), args.cpu_seconds, unit, pool_args, scale)
     print(json.dumps(result), flush=True)
 
 
@@ -827,41 +845,75 @@ def cpu_rows(cfg, L, B, k, n_docs, blk_off, dsc, ids, kbar, vbar, q, ck, cv, cl,
     return out
 
 
-def cpu_baseline(cfg, n_blk, blk_off, seconds):
-    """The fp64 oracle's routing scan on a bounded sample of the same memory (layer 0, the
-    first documents, the same query), one thread, scaled to GB/s of route keys scanned."""
+def cpu_baseline(cfg, di, blk_off, seconds, unit, pool_args, scale):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload, its documents
+    split over the host's cores (orc_doc_scores_mt / orc_pool_mt: threads over contiguous
+    document ranges, each running the single-threaded oracle), reported in the line's unit.
+
+    Pre-pooled memories: the routing scan of whole layers (every document) for whole queries,
+    layer 0 first, until about `seconds` have passed (one full layer at least).  Per-token
+    memories: the oracle's whole path for one layer at a time (pooling of K, V and Kr, scan,
+    top-k, gather, decode of query 0), layers until about `seconds` have passed."""
     import numpy as np
+    import torch
 
     import oracle as O
     from synth import synth as S
 
-    mem = S.memory_config(cfg)
-    q = S.qr_host(cfg, 0)[0, :cfg.T]
-    # calibrate on a few documents, then size the sample to ~`seconds`
-    def run(n_docs):
-        nb = int(blk_off[n_docs])
-        if cfg.per_token:
-            return None
-        rows = S.rows_host(mem.seed, S.S_KRBAR, 0, n_blk, 0, nb)
-        nrows, nq = S.needle_row_table(mem, blk_off)
-        sel = nrows < nb
-        if sel.any():
-            qmem = S.qr_host(mem, 0).reshape(-1, 8, 128)
-            rows[nrows[sel]] = S.needle_rows_host(mem.seed, 0, n_blk, nrows[sel], qmem[nq[sel]])
-        t = time.perf_counter()
-        O.doc_scores(q, rows, blk_off[: n_docs + 1])
-        return nb, time.perf_counter() - t
-
-    if cfg.per_token:
-        return None
-    nb, dt = run(20)
-    n_docs = int(min(len(blk_off) - 1, max(20, 20 * seconds / max(dt, 1e-6))))
-    nb, dt = run(n_docs)
-    gbps = nb * SCAN_BYTES_PER_BLOCK_LAYER / dt / 1e9
-    return {"value": round(gbps, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "fp64 oracle routing scan of layer 0, documents 0..%d (%d blocks) of the same memory, "
-                      "same %d-token query, single thread, %.1f s" % (n_docs - 1, nb, cfg.T, dt),
-            "blocks_per_s": round(nb / dt, 1)}
+    threads = O.host_threads()
+    u16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    if not cfg.per_token:
+        rows = di.prepooled_route_rows_layer_host(0)
+        q = S.qr_host(cfg, 0)
+        n_blk = int(blk_off[-1])
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            O.doc_scores_mt(q[done, :cfg.T], rows, blk_off, threads=threads)
+            done += 1
+            dt = time.perf_counter() - t0
+            if done >= cfg.B or dt + dt / done > seconds:
+                break
+        work = "routing scan of layer 0, all %d documents (%d blocks), query%s 0..%d (%d tokens each)" % (
+            len(blk_off) - 1, n_blk, "" if done == 1 else "s", done - 1, cfg.T)
+        if unit == "TFLOP/s":
+            v = 2.0 * cfg.T * 1024 * n_blk * done / dt / 1e12
+        else:
+            v = n_blk * SCAN_BYTES_PER_BLOCK_LAYER * done / dt / 1e9
+        return {"value": round(v, 6), "unit": unit, "cores": threads, "kind": "oracle",
+                "sample": "fp64 oracle, %s, %d threads, %.1f s" % (work, threads, dt),
+                "blocks_per_s": round(n_blk * done / dt, 1)}
+    # per-token memory: the oracle's own path, layer by layer
+    kt, vt, krt_, tok_d = pool_args[0], pool_args[1], pool_args[2], pool_args[3]
+    tok = tok_d.cpu().numpy()
+    blk, n_blk, _ = O.block_offsets(tok)
+    n_tok = int(tok[-1])
+    q, lk, lv, ll = di.decode_inputs()
+    qr = di.qr()
+    t_total, layers = 0.0, 0
+    for l in range(cfg.n_layers):
+        xs = [u16(a[l:l + 1]) for a in (kt, vt, krt_)]
+        qr_l, q_l = u16(qr[l, 0]), u16(q[l, 0])
+        nl = int(ll[l, 0])
+        lk_l, lv_l = u16(lk[l, 0, :nl]), u16(lv[l, 0, :nl])
+        t0 = time.perf_counter()
+        kb, vb, rb = (O.pool_mt(x, tok, blk, threads=threads)[0] for x in xs)
+        S_o = O.doc_scores_mt(qr_l, rb, blk, threads=threads)
+        ids, _ = O.topk(S_o, cfg.k)
+        ck, cv = O.gather(ids, blk, kb, vb)
+        O.decode(q_l, ck, cv, lk_l, lv_l, scale)
+        t_total += time.perf_counter() - t0
+        layers += 1
+        if t_total + t_total / layers > seconds:
+            break
+    work = ("whole path (pooling of K, V, Kr; scan; top-%d; gather; decode of query 0) of layer%s 0..%d, "
+            "%d tokens per layer" % (cfg.k, "" if layers == 1 else "s", layers - 1, n_tok))
+    if unit == "ms":
+        v = t_total * 1e3 / layers * cfg.n_layers
+    else:
+        v = n_tok * layers / t_total
+    return {"value": round(v, 4 if unit == "ms" else 1), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": "fp64 oracle, %s, %d threads, %.1f s" % (work, threads, t_total)}
 
 
 if __name__ == "__main__":

@@ -2,11 +2,13 @@
  * msa_oracle.c -- plain fp64 CPU reference of the MSA hot path.
  * TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline leg of the bench).
  * Definitions and sources are documented in msa_oracle.h.
- * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math; plain C99).
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared -pthread (no fast-math; plain C99).
  */
+#define _POSIX_C_SOURCE 200809L
 #include "msa_oracle.h"
 
 #include <math.h>
+#include <pthread.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -45,12 +47,16 @@ uint16_t orc_bf16_from_double(double x)
 
 void orc_group_ids(const int64_t* doc_ids, int64_t n, int64_t* group_ids)
 {
-    /* [P2 5.3]: mark where consecutive ids differ, running-sum the marks,
-     * start from 0, then add 1. */
-    int64_t g = 0;
-    for (int64_t i = 0; i < n; ++i) {
-        if (i > 0 && doc_ids[i] != doc_ids[i - 1]) g += 1;
-        group_ids[i] = g + 1;
+    /* [P2 5.3] The tokens of one document are consecutive, so the document ids form
+     * maximal runs of equal values; every run is one group, and the groups are
+     * numbered 1, 2, 3, ... in the order the runs appear. */
+    int64_t run = 0;
+    int64_t i = 0;
+    while (i < n) {
+        int64_t j = i;
+        run += 1;
+        while (j < n && doc_ids[j] == doc_ids[i]) group_ids[j++] = run;
+        i = j;
     }
 }
 
@@ -160,6 +166,102 @@ void orc_doc_scores(int32_t T, const uint16_t* qr, const uint16_t* krbar,
             }
         S[d] = best;
     }
+}
+
+/* ------------------------------------------------- threaded drivers (no arithmetic)
+ * The documents are cut into contiguous ranges of about equal work and each
+ * thread runs the unchanged single-threaded function on one range.  Offsets are
+ * absolute indices into the row arrays, so a range is the same call on a slice of
+ * the offset table; every output value is produced by the same code, in the same
+ * operation order, as in one single-threaded call. */
+
+typedef struct {
+    int kind;                                   /* 0: doc scores, 1: pooling */
+    int32_t T, n_layers, n_docs;
+    const uint16_t *qr, *krbar, *x;
+    int64_t n_tok, n_blk;
+    const int64_t *doc_tok_off, *doc_blk_off;   /* already offset to the range's first doc */
+    double* S;
+    uint16_t* xbar;
+} orc_range;
+
+static void* orc_run_range(void* arg)
+{
+    orc_range* r = (orc_range*)arg;
+    if (r->n_docs <= 0) return NULL;
+    if (r->kind == 0)
+        orc_doc_scores(r->T, r->qr, r->krbar, r->doc_blk_off, r->n_docs, r->S);
+    else
+        orc_pool(r->n_layers, r->x, r->n_tok, r->doc_tok_off, r->doc_blk_off, r->n_docs, r->n_blk, r->xbar);
+    return NULL;
+}
+
+/* First document of range i of n when work[d] = off[d+1] - off[d] is split evenly. */
+static int32_t orc_range_start(const int64_t* off, int32_t n_docs, int32_t i, int32_t n)
+{
+    if (i <= 0) return 0;
+    if (i >= n) return n_docs;
+    int64_t target = off[0] + (int64_t)((double)(off[n_docs] - off[0]) * i / n);
+    int32_t lo = 0, hi = n_docs;                 /* first d with off[d] >= target */
+    while (lo < hi) {
+        int32_t mid = lo + (hi - lo) / 2;
+        if (off[mid] < target) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+static void orc_run_ranges(orc_range base, const int64_t* split_off, int32_t n_docs, int32_t n_threads)
+{
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > 256) n_threads = 256;
+    orc_range rs[256];
+    pthread_t th[256];
+    int started[256];
+    for (int32_t i = 0; i < n_threads; ++i) {
+        int32_t d0 = orc_range_start(split_off, n_docs, i, n_threads);
+        int32_t d1 = orc_range_start(split_off, n_docs, i + 1, n_threads);
+        rs[i] = base;
+        rs[i].n_docs = d1 - d0;
+        rs[i].doc_blk_off = base.doc_blk_off + d0;
+        if (base.doc_tok_off) rs[i].doc_tok_off = base.doc_tok_off + d0;
+        if (base.S) rs[i].S = base.S + d0;
+        started[i] = i > 0 && pthread_create(&th[i], NULL, orc_run_range, &rs[i]) == 0;
+        if (i > 0 && !started[i]) orc_run_range(&rs[i]);   /* no thread: run it here */
+    }
+    orc_run_range(&rs[0]);
+    for (int32_t i = 1; i < n_threads; ++i)
+        if (started[i]) pthread_join(th[i], NULL);
+}
+
+void orc_doc_scores_mt(int32_t T, const uint16_t* qr, const uint16_t* krbar,
+                       const int64_t* doc_blk_off, int32_t n_docs, double* S, int32_t n_threads)
+{
+    orc_range b;
+    memset(&b, 0, sizeof b);
+    b.kind = 0;
+    b.T = T;
+    b.qr = qr;
+    b.krbar = krbar;
+    b.doc_blk_off = doc_blk_off;
+    b.S = S;
+    orc_run_ranges(b, doc_blk_off, n_docs, n_threads);
+}
+
+void orc_pool_mt(int32_t n_layers, const uint16_t* x, int64_t n_tok,
+                 const int64_t* doc_tok_off, const int64_t* doc_blk_off, int32_t n_docs,
+                 int64_t n_blk, uint16_t* xbar, int32_t n_threads)
+{
+    orc_range b;
+    memset(&b, 0, sizeof b);
+    b.kind = 1;
+    b.n_layers = n_layers;
+    b.x = x;
+    b.n_tok = n_tok;
+    b.n_blk = n_blk;
+    b.doc_tok_off = doc_tok_off;
+    b.doc_blk_off = doc_blk_off;
+    b.xbar = xbar;
+    orc_run_ranges(b, doc_tok_off, n_docs, n_threads);
 }
 
 /* ------------------------------------------------------------------ top-k */

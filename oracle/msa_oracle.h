@@ -7,7 +7,9 @@
  * header, table or helper with the GPU library; neither side includes the other.
  *
  * Every function is a direct, unblocked, single-threaded transcription of the
- * definition it cites.  Floating point is fp64 over the exact values of the
+ * definition it cites.  The two *_mt functions are drivers with no arithmetic of
+ * their own: they run the single-threaded function on contiguous document ranges
+ * in parallel threads, so their outputs are those of one single-threaded call.  Floating point is fp64 over the exact values of the
  * bf16 inputs; the only roundings are the ones the definition itself contains
  * (the pooled means are stored as bf16, round-to-nearest-even).
  *
@@ -30,6 +32,7 @@
  *   orc_pool                                    pinned (constant block, 1-token tail, {a,-a}, hand case)
  *   orc_head_norms                              pinned (library norm on exact inputs)
  *   orc_block_score / orc_doc_scores            pinned (scale invariance, +-1, orthogonal, library cosine, superset)
+ *   orc_doc_scores_mt, orc_pool_mt              pinned (bit-identical to the single-threaded calls)
  *   orc_topk                                    pinned (brute-force sort, ties, permutation)
  *   orc_gather                                  pinned (library concatenation)
  *   orc_decode                                  pinned (single key, equal keys, q=0, library softmax, permutation)
@@ -57,9 +60,9 @@ double orc_bf16_to_double(uint16_t b);
 /* Nearest bf16 to x, ties to even (no intermediate float rounding). */
 uint16_t orc_bf16_from_double(double x);
 
-/* [P2 5.3] map_tensor_to_group_ids: a run-length sequence of per-token
- * document ids -> 1-based consecutive group ids (a new group starts wherever
- * the id changes).  Writes n values into group_ids. */
+/* [P2 5.3, the document-id to group-id mapping] Per-token document ids, whose
+ * tokens are consecutive per document, -> 1-based group ids: each maximal run of
+ * equal ids is one group, numbered in order of appearance.  Writes n values. */
 void orc_group_ids(const int64_t* doc_ids, int64_t n, int64_t* group_ids);
 
 /* Token offsets of the groups found by orc_group_ids: doc_tok_off[g] is the
@@ -95,6 +98,18 @@ double orc_block_score(const uint16_t* q_row, const uint16_t* k_row);
  * qr: [T][8][128]; krbar: [n_blk][8][128]; S: [n_docs]. */
 void orc_doc_scores(int32_t T, const uint16_t* qr, const uint16_t* krbar,
                     const int64_t* doc_blk_off, int32_t n_docs, double* S);
+
+/* orc_doc_scores over n_threads threads (each runs orc_doc_scores on a contiguous
+ * range of documents of about equal block count); S is identical to one
+ * orc_doc_scores call.  A thread that cannot be started runs in the caller. */
+void orc_doc_scores_mt(int32_t T, const uint16_t* qr, const uint16_t* krbar,
+                       const int64_t* doc_blk_off, int32_t n_docs, double* S, int32_t n_threads);
+
+/* orc_pool over n_threads threads (contiguous document ranges of about equal token
+ * count); xbar is identical to one orc_pool call. */
+void orc_pool_mt(int32_t n_layers, const uint16_t* x, int64_t n_tok,
+                 const int64_t* doc_tok_off, const int64_t* doc_blk_off, int32_t n_docs,
+                 int64_t n_blk, uint16_t* xbar, int32_t n_threads);
 
 /* [P1 架构; P2 3.3.2 doc_top_k; P5 方法拆解] Top-k documents: the k largest S,
  * ordered by (S descending, id ascending).  ids[k], scores[k]. */

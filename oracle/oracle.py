@@ -25,7 +25,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle with gcc (plain C99, fp64, no FMA contraction)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+        subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
                                "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
@@ -56,6 +56,8 @@ def lib():
         L.orc_block_score.argtypes = [P, P]
         L.orc_block_score.restype = f64
         L.orc_doc_scores.argtypes = [i32, P, P, P, i32, P]
+        L.orc_doc_scores_mt.argtypes = [i32, P, P, P, i32, P, i32]
+        L.orc_pool_mt.argtypes = [i32, P, i64, P, P, i32, i64, P, i32]
         L.orc_topk.argtypes = [P, i32, i32, P, P]
         L.orc_gather.argtypes = [P, i32, P, P, P, P, P]
         L.orc_gather.restype = i64
@@ -138,6 +140,27 @@ def pool(x, doc_tok_off, doc_blk_off) -> np.ndarray:
     return out
 
 
+def host_threads() -> int:
+    """Worker threads for the threaded drivers: the CPUs this process may run on, at most 16
+    (the host share of one GPU on the machines this runs on)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def pool_mt(x, doc_tok_off, doc_blk_off, threads: int = None) -> np.ndarray:
+    """pool() with the documents split over threads (identical output)."""
+    x = _u16(x)
+    L, n_tok = x.shape[0], x.shape[1]
+    t, b = _i64(doc_tok_off), _i64(doc_blk_off)
+    n_docs, n_blk = t.size - 1, int(b[-1])
+    out = np.zeros((L, n_blk, H, D), np.uint16)
+    lib().orc_pool_mt(L, _p(x), n_tok, _p(t), _p(b), n_docs, n_blk, _p(out), threads or host_threads())
+    return out
+
+
 def head_norms(rows) -> np.ndarray:
     """rows: [..., 8, 128] uint16 -> [..., 8] float64."""
     rows = _u16(rows)
@@ -161,6 +184,27 @@ def doc_scores(qr, krbar, doc_blk_off) -> np.ndarray:
     T, n_docs = q.shape[0], b.size - 1
     S = np.empty(n_docs, np.float64)
     lib().orc_doc_scores(T, _p(q), _p(k), _p(b), n_docs, _p(S))
+    return S
+
+
+def doc_scores_mt(qr, krbar, doc_blk_off, threads: int = None, chunks: int = 1, progress=None) -> np.ndarray:
+    """doc_scores() with the documents split over threads (identical output).  With chunks > 1
+    the documents are processed in that many consecutive pieces of about equal block count and
+    progress(i, chunks) is called after piece i."""
+    q, k, b = _u16(qr), _u16(krbar), _i64(doc_blk_off)
+    T, n_docs = q.shape[0], b.size - 1
+    assert k.shape[0] >= int(b[-1]), "krbar holds fewer rows than the offsets name"
+    S = np.empty(n_docs, np.float64)
+    threads = threads or host_threads()
+    chunks = max(1, min(chunks, max(n_docs, 1)))
+    total = int(b[-1] - b[0])
+    starts = [int(np.searchsorted(b[:-1], b[0] + total * i // chunks, side="left")) for i in range(chunks)] + [n_docs]
+    for i in range(chunks):
+        d0, d1 = starts[i], max(starts[i], starts[i + 1])
+        if d1 > d0:
+            lib().orc_doc_scores_mt(T, _p(q), _p(k), _p(b[d0:]), d1 - d0, _p(S[d0:]), threads)
+        if progress is not None:
+            progress(i + 1, chunks)
     return S
 
 
@@ -249,5 +293,6 @@ def encode(x, w_k, w_v, w_kr, w_norm, eps: float, theta: float, doc_tok_off, doc
 
 
 __all__ = ["build", "lib", "bf16_to_f64", "bf16_from_f64", "bf16_from_f64_scalar", "group_ids",
-           "doc_tok_offsets", "block_offsets", "pool", "head_norms", "block_score", "doc_scores",
+           "doc_tok_offsets", "block_offsets", "pool", "pool_mt", "head_norms", "block_score", "doc_scores",
+           "doc_scores_mt", "host_threads",
            "doc_scores_all", "topk", "gather", "decode", "prefill", "encode", "H", "D", "BLOCK", "ROW"]

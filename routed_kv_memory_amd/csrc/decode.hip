@@ -29,9 +29,6 @@ constexpr int kWaveRows = 32;                          // per wave
 constexpr int kRowsPerSplit = kWaveRows * kSplitWaves;  // per workgroup
 constexpr int kVStride = kDim + 8;        // bf16 per staged V row
 
-#ifndef MSA_DECODE_LOAD
-#define MSA_DECODE_LOAD(p) __builtin_nontemporal_load(p)   // rows are read once
-#endif
 
 template <int G>
 __global__ void __launch_bounds__(64 * kSplitWaves)
@@ -83,8 +80,8 @@ decode_split_kernel(int32_t Hq, const uint16_t* __restrict__ q, const uint16_t* 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int32_t r = active ? w0 + 4 * i + g : r_begin;
-    kr[i] = MSA_DECODE_LOAD(reinterpret_cast<const u32x4*>(row_ptr(ck, lk, r) + 8 * j));
-    vr[i] = MSA_DECODE_LOAD(reinterpret_cast<const u32x4*>(row_ptr(cv, lv, r) + 8 * j));
+    kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row_ptr(ck, lk, r) + 8 * j));
+    vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row_ptr(cv, lv, r) + 8 * j));
   }
   // Q^T as the B operand: column j = head j of the group (zero past G), dims 32 s + 8 g .. +7
   bf16x8 qf[4];

@@ -14,22 +14,24 @@
 // row j, k 8 g .. 8 g + 7 -- is 16 contiguous bytes per lane in either operand.
 //
 // Work: one 512-thread workgroup per (4 consecutive blocks = 256 token rows, pair of
-// output heads = 256 columns of K, V or Kr).  The hidden dimension is walked in 32-wide
-// chunks (one MFMA k step); a chunk is 16 row fragments and 16 column fragments of
-// 1 KiB, and it reaches LDS by direct global->LDS loads (global_load_lds_dwordx4: a
-// wave instruction writes 64 lanes x 16 B contiguously, i.e. exactly one fragment in the
-// lane-major order the operand reads want), through a ring of 4 stages, 3 chunks ahead,
-// with no staging registers.  Each wave loads 4 of a chunk's fragments and waits for its
-// own loads of a chunk before the barrier that publishes it; the barrier also retires
-// every wave's reads of the stage the next loads overwrite.  Wave (wr, wc) accumulates
-// block wr (64 rows) x head wc of the pair (128 columns): 4 x 8 accumulator tiles, kept
-// in VGPRs (the library is built with MFMA's VGPR form).  The epilogue stays in
-// registers: a row's 128 columns sit in the 16 lanes of a DPP row (per-row mean square by
-// a row reduction), columns e and e + 64 of a head are in the same lane (the rotation
-// needs no exchange), and a block mean is an in-lane sum over 16 rows plus a sum over the
-// 4 lane groups.  Workgroups are placed so that those an XCD runs together share 4 head
-// pairs' weights and 8 row groups' hidden rows through its L2.  Rows past a block's end (or the last token) are
-// loaded from a clamped, in-bounds row and never enter a mean.
+// output heads = 256 columns of K, V or Kr).  The hidden dimension is walked in 64-wide
+// chunks (two MFMA k steps).  A chunk of the 256 hidden rows and of the 256 weight rows
+// (32 KiB each, 128 bytes of every row) reaches LDS by direct global->LDS loads
+// (global_load_lds_dwordx4: one wave instruction writes 64 lanes x 16 B contiguously),
+// each instruction covering 8 rows x one whole 128-byte line, with no staging registers.
+// Within a row the eight 16-byte segments are XOR-permuted by the row's index in its
+// group of 8, so that fragment reads (16 rows, one segment each) spread over all banks.
+// Two stages of 64 KiB alternate: the next chunk's loads go out right after the barrier
+// that publishes the current one, and each wave waits for its own loads of a chunk
+// before that barrier.  Wave (wr, wc) accumulates block wr (64 rows) x head wc of the
+// pair (128 columns): 4 x 8 accumulator tiles, kept in VGPRs (the library is built with
+// MFMA's VGPR form).  The epilogue stays in registers: a row's 128 columns sit in the 16
+// lanes of a DPP row (per-row mean square by a row reduction), columns e and e + 64 of a
+// head are in the same lane (the rotation needs no exchange), and a block mean is an
+// in-lane sum over 16 rows plus a sum over the 4 lane groups.  Workgroups are placed so
+// that those an XCD runs together share 4 head pairs' weights and 8 row groups' hidden
+// rows through its L2.  Rows past a block's end (or the last token) are loaded from a
+// clamped, in-bounds row and never enter a mean.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -38,10 +40,7 @@ namespace {
 
 constexpr int kEncBlocks = 4;                  // blocks per workgroup (= 256 token rows)
 constexpr int kPairs = 3 * kHeads / 2;         // head pairs: K 0-3, V 4-7, Kr 8-11
-#ifndef MSA_ENCODE_RUN_PAIRS
-#define MSA_ENCODE_RUN_PAIRS 4
-#endif
-constexpr int kRunPairs = MSA_ENCODE_RUN_PAIRS;   // head pairs in a run of 32 workgroups on one XCD
+constexpr int kRunPairs = 4;                   // head pairs in a run of 32 workgroups on one XCD
 constexpr int kRunGroups = 32 / kRunPairs;        // row groups in a run
 constexpr int kKC = 64;                        // hidden columns per staged chunk (128 B of a row)
 constexpr int kRegionKB = 32;                  // per chunk: 256 rows (or columns) x 128 B = 32 KiB

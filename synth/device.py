@@ -108,6 +108,23 @@ class DeviceInputs:
                 self.gen.plant(staging, 0, mem.n_blk, l, r_d, q_d, qr[l], mem.seed)
             yield l, staging
 
+    def prepooled_route_rows_layer_host(self, layer: int) -> np.ndarray:
+        """Row-major routing keys of one layer, needles planted, as a host array
+        [N_blk][8][128] uint16 (generated on the device, then copied)."""
+        mem = self.mem
+        off = S.prepooled_doc_blk_offsets(mem)
+        rows, qrows = S.needle_row_table(mem, off)
+        staging = torch.empty((mem.n_blk, S.H, S.D), dtype=torch.bfloat16, device=self.device)
+        self.gen.fill(staging, mem.seed, S.S_KRBAR, layer * mem.n_blk * S.ROW)
+        if rows.size:
+            qr = self.mem_qr()
+            self.gen.plant(staging, 0, mem.n_blk, layer, _i64(rows, self.device), _i64(qrows, self.device),
+                           qr[layer], mem.seed)
+            del qr
+        out = staging.view(torch.int16).cpu().numpy().view(np.uint16)
+        del staging
+        return out
+
     # ------------------------------------------------------------------ decode
     def decode_inputs(self):
         """q [L][B][Hq][128], loc_k/loc_v [L][B][L_loc][8][128] bf16, loc_len [L][B] int32."""

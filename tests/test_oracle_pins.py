@@ -273,6 +273,31 @@ def test_appending_query_rows_never_lowers_scores(orc):
                           np.maximum(s_small, orc.doc_scores(q[2:], k, off))[[0, 2, 3]])
 
 
+@pytest.mark.parametrize("threads", [1, 2, 3, 7, 64])
+def test_threaded_doc_scores_equal_single_threaded(orc, threads):
+    # ragged documents, empty ones at both ends and in the middle, more threads than documents
+    rng = np.random.default_rng(13)
+    counts = np.array([0, 3, 1, 0, 0, 17, 2, 9, 1, 1, 0, 40, 5, 0])
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    q = rand_bf16(rng, (5, H, D))
+    k = rand_bf16(rng, (int(off[-1]), H, D))
+    ref = orc.doc_scores(q, k, off)
+    got = orc.doc_scores_mt(q, k, off, threads=threads)
+    assert np.array_equal(got, ref)                 # bit-identical, -inf for empty documents
+    got = orc.doc_scores_mt(q, k, off, threads=threads, chunks=4, progress=lambda i, n: None)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("threads", [1, 4, 9])
+def test_threaded_pool_equals_single_threaded(orc, threads):
+    rng = np.random.default_rng(14)
+    lens = np.array([65, 0, 1, 130, 64, 7, 200])
+    tok = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    blk, _, _ = orc.block_offsets(tok)
+    x = rand_bf16(rng, (2, int(tok[-1]), H, D))
+    assert np.array_equal(orc.pool_mt(x, tok, blk, threads=threads), orc.pool(x, tok, blk))
+
+
 # -------------------------------------------------------------------- top-k
 
 def _selection_topk(S, k):
