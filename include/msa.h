@@ -111,7 +111,9 @@ int64_t msa_route_tiles(int64_t n_blk);
  * (tokens [doc_tok_off[d], doc_tok_off[d+1])) and block j of d, the block covers
  * tokens [s_d + 64 j, min(s_d + 64 j + 64, e_d)) and its value is the mean over
  * those real tokens (a final partial block is averaged over its own tokens),
- * accumulated in fp32 and rounded to bf16 (nearest-even).  Applied to K, V and Kr.
+ * accumulated in fp64 (exact for sums of up to 64 bf16 values whose magnitudes span
+ * less than 2^39), divided in fp64 and rounded once to bf16 (nearest-even).  Applied
+ * to K, V and Kr.
  *
  *   k, v, kr       [n_layers][n_tok][8][128] bf16, per-token inputs
  *   doc_tok_off    [n_docs + 1] int64, device

@@ -7,14 +7,17 @@
 // "【MSA】突破100M Token 上下文…", 3.3.2; xiaohongrsx.github.io "MSA paper reading",
 // 方法拆解).
 //
-// One 512-thread workgroup pools one 16-block tile of one layer; wave w pools
-// blocks w and w + 8.  Lane l owns 16-byte chunks l and 64 + l of each 2 KiB token
-// row, so every row is two contiguous 1 KiB wave loads (nontemporal: each input
-// byte is read once), four tokens in flight per step, summed in fp32 in registers.
-// The tile's outputs (K-bar and V-bar rows, routing keys in the route layout) are
-// staged in LDS and written as three contiguous 32 KiB runs at the end: writes
-// interleaved finely with the read stream, and the route layout's scattered
-// 16-byte pieces, cost far more HBM time than their size.
+// One 256-thread workgroup pools one of the three tensors (K, V or Kr) over one 16-block
+// tile of one layer; wave w pools blocks w, w + 4, w + 8 and w + 12 in turn.  Lane l owns
+// 16-byte chunks l and 64 + l of each 2 KiB token row, so a row is two contiguous 1 KiB
+// wave loads (nontemporal: every input byte is read once), eight tokens in flight per
+// step.  Sums are accumulated in fp64: a sum of at most 64 bf16 values is exact there
+// unless their magnitudes span more than 2^39, so the mean is the exactly rounded fp64
+// quotient, rounded once more to bf16 (nearest-even) straight from fp64.  K-bar and
+// V-bar rows go to HBM from registers (one contiguous 2 KiB row per block); the routing
+// keys, whose route layout scatters a block over 16-byte pieces, are staged in LDS and
+// written as one contiguous 32 KiB run per tile.  Small register and LDS footprints
+// (32 KiB per workgroup) let four workgroups share a CU, so 16 waves keep loads in flight.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -38,42 +41,72 @@ __device__ __forceinline__ uint4 ld_nt(const uint4* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-__device__ __forceinline__ void add8(float* acc, uint4 w) {
-  acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
-  acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
-  acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
-  acc[6] += bf16_lo(w.w); acc[7] += bf16_hi(w.w);
+__device__ __forceinline__ void add8(double* acc, uint4 w) {
+  acc[0] += (double)bf16_lo(w.x); acc[1] += (double)bf16_hi(w.x);
+  acc[2] += (double)bf16_lo(w.y); acc[3] += (double)bf16_hi(w.y);
+  acc[4] += (double)bf16_lo(w.z); acc[5] += (double)bf16_hi(w.z);
+  acc[6] += (double)bf16_lo(w.w); acc[7] += (double)bf16_hi(w.w);
 }
 
-// Rounds acc/n to bf16, returns the packed 8 values and adds their squares to *ss.
-__device__ __forceinline__ uint4 mean8(const float* acc, float n, float* ss) {
+// fp64 -> bf16 bits, round to nearest even, straight from the double (no intermediate
+// fp32 rounding).  Finite inputs; beyond the largest finite bf16 gives infinity.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
+  uint32_t r;
+  if (a >= ((uint64_t)(1023 - 126) << 52)) {
+    // normal range: keep 7 of the 52 fraction bits, nearest-even on the 45 dropped ones
+    // (a carry moves into the exponent), then rebias the exponent from 1023 to 127
+    const uint64_t q = (a + ((1ull << 44) - 1) + ((a >> 45) & 1ull)) >> 45;
+    r = (uint32_t)(q - ((uint64_t)(1023 - 127) << 7));
+    if (r > 0x7F80u) r = 0x7F80u;
+  } else {
+    // below 2^-126: multiples of 2^-133; the scaling is exact and rint rounds to even
+    r = (uint32_t)__builtin_rint(__longlong_as_double((long long)a) * 0x1p133);
+  }
+  return sign | r;
+}
+
+// Rounds acc / n to bf16 and packs 8 values; adds the squares of the rounded values to *ss.
+__device__ __forceinline__ uint4 mean8(const double* acc, int32_t n, float* ss) {
+  double m[8];
+  if (n == kBlockTokens) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = acc[i] * (1.0 / kBlockTokens);   // exact: a power of two
+  } else {
+    const double dn = (double)n;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = acc[i] / dn;                     // correctly rounded
+  }
   uint32_t p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t lo = f32_to_bf16_rne(acc[2 * i] / n);
-    uint32_t hi = f32_to_bf16_rne(acc[2 * i + 1] / n);
-    if (ss) {
-      float a = __uint_as_float(lo << 16), b = __uint_as_float(hi << 16);
-      *ss += a * a + b * b;
-    }
+    const uint32_t lo = f64_to_bf16_rne(m[2 * i]);
+    const uint32_t hi = f64_to_bf16_rne(m[2 * i + 1]);
+    const float a = __uint_as_float(lo << 16), b = __uint_as_float(hi << 16);
+    *ss += a * a + b * b;
     p[i] = lo | (hi << 16);
   }
   return make_uint4(p[0], p[1], p[2], p[3]);
 }
 
-constexpr int kU = 4;   // tokens per unrolled step
+constexpr int kPoolWaves = 4;              // waves per workgroup
+constexpr int kPoolWG = 64 * kPoolWaves;
+constexpr int kU = 8;                      // tokens in flight per wave step
 
-__global__ void __launch_bounds__(512) pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
-                                                   const uint4* __restrict__ kr, int64_t n_tok,
-                                                   const int64_t* __restrict__ tok_off,
-                                                   const int64_t* __restrict__ blk_off, int32_t n_docs,
-                                                   int64_t n_blk, int64_t tiles, uint4* __restrict__ kbar,
-                                                   uint4* __restrict__ vbar, uint4* __restrict__ krt,
-                                                   float* __restrict__ krn) {
+__global__ void __launch_bounds__(kPoolWG) pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
+                                                       const uint4* __restrict__ kr, int64_t n_tok,
+                                                       const int64_t* __restrict__ tok_off,
+                                                       const int64_t* __restrict__ blk_off, int32_t n_docs,
+                                                       int64_t n_blk, int64_t tiles, uint4* __restrict__ kbar,
+                                                       uint4* __restrict__ vbar, uint4* __restrict__ krt,
+                                                       float* __restrict__ krn) {
   __shared__ int64_t s_t0[kTile];
   __shared__ int32_t s_n[kTile];
-  __shared__ uint4 s_out[3][kTileElems / 8];   // the tile's K-bar, V-bar rows and route-layout keys
-  const int64_t tile = blockIdx.x;
+  __shared__ uint4 s_route[kTileElems / 8];   // the tile's pooled routing keys, route layout
+  const int tensor = (int)(blockIdx.x % 3u);  // 0: K, 1: V, 2: Kr (uniform per workgroup)
+  const int64_t tile = blockIdx.x / 3u;
   const int64_t layer = blockIdx.y;
   const int tid = threadIdx.x;
   if (tid < kTile) {
@@ -96,66 +129,48 @@ __global__ void __launch_bounds__(512) pool_kernel(const uint4* __restrict__ k, 
   __syncthreads();
 
   const int wave = tid >> 6, lane = tid & 63;
-  const uint4* kl = k + layer * n_tok * (kRow / 8);
-  const uint4* vl = v + layer * n_tok * (kRow / 8);
-  const uint4* rl = kr + layer * n_tok * (kRow / 8);
-  for (int b = wave; b < kTile; b += 8) {
+  const uint4* src = (tensor == 0 ? k : tensor == 1 ? v : kr) + layer * n_tok * (kRow / 8);
+  uint4* dst = tensor == 0 ? kbar : vbar;
+  for (int b = wave; b < kTile; b += kPoolWaves) {
     const int64_t blk = tile * kTile + b;
     const int64_t t0 = s_t0[b];
     const int32_t n = s_n[b];
-    float ak[2][8] = {}, av[2][8] = {}, ar[2][8] = {};
+    double acc[2][8] = {};
     int32_t t = 0;
     for (; t + kU <= n; t += kU) {
-      uint4 wk[kU][2], wv[kU][2], wr[kU][2];
+      uint4 w[kU][2];
 #pragma unroll
       for (int u = 0; u < kU; ++u)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int64_t row = (t0 + t + u) * (kRow / 8) + hh * 64 + lane;
-          wk[u][hh] = ld_nt(kl + row); wv[u][hh] = ld_nt(vl + row); wr[u][hh] = ld_nt(rl + row);
-        }
+        for (int hh = 0; hh < 2; ++hh) w[u][hh] = ld_nt(src + (t0 + t + u) * (kRow / 8) + hh * 64 + lane);
 #pragma unroll
       for (int u = 0; u < kU; ++u)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) { add8(ak[hh], wk[u][hh]); add8(av[hh], wv[u][hh]); add8(ar[hh], wr[u][hh]); }
+        for (int hh = 0; hh < 2; ++hh) add8(acc[hh], w[u][hh]);
     }
     for (; t < n; ++t)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int64_t row = (t0 + t) * (kRow / 8) + hh * 64 + lane;
-        add8(ak[hh], ld_nt(kl + row)); add8(av[hh], ld_nt(vl + row)); add8(ar[hh], ld_nt(rl + row));
-      }
+      for (int hh = 0; hh < 2; ++hh) add8(acc[hh], ld_nt(src + (t0 + t) * (kRow / 8) + hh * 64 + lane));
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int c16 = hh * 64 + lane;   // chunk of the row: head c16 / 16, dims (c16 % 16) * 8
-      const int h = c16 >> 4, c = c16 & 15;
       float ss = 0.f;
-      uint4 ok = make_uint4(0, 0, 0, 0), ov = ok, orr = ok;
-      if (n > 0) {
-        const float fn = (float)n;
-        ok = mean8(ak[hh], fn, nullptr);
-        ov = mean8(av[hh], fn, nullptr);
-        orr = mean8(ar[hh], fn, &ss);
+      uint4 o = make_uint4(0, 0, 0, 0);
+      if (n > 0) o = mean8(acc[hh], n, &ss);
+      if (tensor < 2) {
+        if (blk < n_blk) dst[(layer * n_blk + blk) * (kRow / 8) + c16] = o;
+      } else {
+        const int h = c16 >> 4, c = c16 & 15;
+        s_route[h * (kTile * 16) + c * kTile + b] = o;   // route layout: [h][c][b][8]
+        ss = row16_sum(ss);   // the 16 lanes of a DPP row hold the 16 chunks of head h
+        if (krn && c == 0) krn[((layer * tiles + tile) * kHeads + h) * kTile + b] = sqrtf(ss);
       }
-      s_out[0][b * (kRow / 8) + c16] = ok;
-      s_out[1][b * (kRow / 8) + c16] = ov;
-      // route layout: [layer][tile][h][c][b][8]
-      s_out[2][h * (kTile * 16) + c * kTile + b] = orr;
-      ss = row16_sum(ss);   // the 16 lanes of a DPP row hold the 16 chunks of head h
-      if (krn && c == 0) krn[((layer * tiles + tile) * kHeads + h) * kTile + b] = sqrtf(ss);
     }
   }
-  __syncthreads();
-  const int64_t nb = n_blk - tile * kTile < kTile ? n_blk - tile * kTile : kTile;   // real blocks in the tile
-  uint4* dk = kbar + (layer * n_blk + tile * kTile) * (kRow / 8);
-  uint4* dv = vbar + (layer * n_blk + tile * kTile) * (kRow / 8);
-  uint4* dr = krt + (layer * tiles + tile) * (kTileElems / 8);
-  for (int i = tid; i < kTileElems / 8; i += 512) {
-    if (i < nb * (kRow / 8)) {
-      dk[i] = s_out[0][i];
-      dv[i] = s_out[1][i];
-    }
-    dr[i] = s_out[2][i];
+  if (tensor == 2) {
+    __syncthreads();
+    uint4* dr = krt + (layer * tiles + tile) * (kTileElems / 8);
+    for (int i = tid; i < kTileElems / 8; i += kPoolWG) dr[i] = s_route[i];
   }
 }
 
@@ -189,7 +204,7 @@ hipError_t launch_pool(int32_t L, const uint16_t* k, const uint16_t* v, const ui
                        uint16_t* kbar, uint16_t* vbar, uint16_t* krt, float* krn, hipStream_t s) {
   const int64_t tiles = route_tiles(n_blk);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)tiles, (unsigned)L), dim3(512), 0, s,
+  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)(3 * tiles), (unsigned)L), dim3(kPoolWG), 0, s,
                      reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
                      reinterpret_cast<const uint4*>(kr), n_tok, doc_tok_off, doc_blk_off, n_docs, n_blk, tiles,
                      reinterpret_cast<uint4*>(kbar), reinterpret_cast<uint4*>(vbar), reinterpret_cast<uint4*>(krt),
