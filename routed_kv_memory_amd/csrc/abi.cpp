@@ -136,7 +136,7 @@ MSA_API int msa_pool_blocks(int32_t n_layers, const uint16_t* k, const uint16_t*
   if (n_layers < 1 || n_docs < 1 || n_tok < 0 || n_blk < 0)
     return fail(MSA_ERR_SHAPE, "msa_pool_blocks: n_layers=%d n_docs=%d n_tok=%lld n_blk=%lld", n_layers, n_docs,
                 (long long)n_tok, (long long)n_blk);
-  if (msa::route_tiles(n_blk) > INT32_MAX) return fail(MSA_ERR_UNSUPPORTED, "msa_pool_blocks: n_blk too large");
+  if (msa::route_tiles(n_blk) > INT32_MAX / 3) return fail(MSA_ERR_UNSUPPORTED, "msa_pool_blocks: n_blk too large");
   return hip_status(msa::launch_pool(n_layers, k, v, kr, n_tok, doc_tok_off, doc_blk_off, n_docs, n_blk, kbar, vbar,
                                      krbar_route, krbar_norm, as_stream(stream)),
                     "msa_pool_blocks");
