@@ -200,6 +200,25 @@ int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
                    int32_t* topk_ids, float* topk_scores, float* doc_scores,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): msa_route_topk with no workspace
+ * argument.  Its scratch (the scores when doc_scores is NULL, and the top-k candidate
+ * buffers) is a fixed array of MSA_NOALLOC_SCRATCH_BYTES in the library's device code
+ * object, one per GPU, held until the process ends; the call itself allocates nothing.
+ * Arguments, layouts and results are those of msa_route_topk.  The caller still owns
+ * the inputs and outputs.
+ * Limit: msa_route_topk_workspace_size(n_layers, B, n_docs, k) must not exceed
+ * MSA_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. 18 layers x 8 queries x 100,000 documents),
+ * else MSA_ERR_WORKSPACE and nothing is launched.  The array is shared by every call on
+ * the same GPU and keeps the last call's contents: calls that overlap on one GPU (on
+ * different streams or threads) race and must be serialised by the caller. */
+#define MSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t msa_route_topk_noalloc_max_scratch(void);
+int msa_route_topk_noalloc(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
+                           const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
+                           const int32_t* blk_doc, int32_t n_docs, int32_t k,
+                           int32_t* topk_ids, float* topk_scores, float* doc_scores, void* stream);
+
 /* ------------------------------------------------------------ A4: context gather
  *
  * [P1 架构 (selected compressed K/V concatenated with the local K/V); P2 5.2;

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "msa_kernels.hpp"
 
@@ -241,6 +242,77 @@ MSA_API int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int3
   if (e != hipSuccess) return hip_status(e, "msa_route_topk (scores)");
   e = msa::launch_topk((int64_t)n_layers * B, scores, n_docs, k, topk_ids, topk_scores, rest, s);
   if (e != hipSuccess) return hip_status(e, "msa_route_topk (top-k)");
+  return MSA_OK;
+}
+
+// ------------------------------------------------- A2 + A3 without allocation
+//
+// Scratch of msa_route_topk_noalloc: one fixed array per GPU, in the library's code
+// object, so the call needs no workspace argument and allocates nothing.  In host code
+// the array's name is only a stand-in: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and that pointer is what the kernels
+// receive.  Every call on a device shares the array; calls that overlap on one device
+// (two streams, two threads) race on it.
+
+static __device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array, looked up on first use.
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "msa_route_topk_noalloc (hipGetDevice)");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_route_topk_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                  "msa_route_topk_noalloc (hipGetSymbolAddress)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+}  // namespace
+
+MSA_API size_t msa_route_topk_noalloc_max_scratch(void) { return MSA_NOALLOC_SCRATCH_BYTES; }
+
+MSA_API int msa_route_topk_noalloc(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
+                                   const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
+                                   const int32_t* blk_doc, int32_t n_docs, int32_t k, int32_t* topk_ids,
+                                   float* topk_scores, float* doc_scores, void* stream) {
+  int st = check_route_args("msa_route_topk_noalloc", n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs);
+  if (st) return st;
+  if (!topk_ids) return fail(MSA_ERR_NULL, "msa_route_topk_noalloc: null pointer");
+  if (k < 1 || k > n_docs) return fail(MSA_ERR_SHAPE, "msa_route_topk_noalloc: k=%d n_docs=%d", k, n_docs);
+  if (k > MSA_MAX_TOPK) return fail(MSA_ERR_UNSUPPORTED, "msa_route_topk_noalloc: k=%d > %d", k, MSA_MAX_TOPK);
+  if ((int64_t)n_layers * B > 65535) return fail(MSA_ERR_UNSUPPORTED, "msa_route_topk_noalloc: n_layers*B > 65535");
+  // the same carving as msa_route_topk: scores (unless the caller keeps them), then top-k
+  const size_t need = msa_route_topk_workspace_size(n_layers, B, n_docs, k);
+  if (need > (size_t)MSA_NOALLOC_SCRATCH_BYTES)
+    return fail(MSA_ERR_WORKSPACE,
+                "msa_route_topk_noalloc: needs %zu bytes of scratch, the fixed maximum is %zu "
+                "(use msa_route_topk with a workspace)", need, (size_t)MSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st) return st;
+  char* base = reinterpret_cast<char*>(ws);
+  float* scores = doc_scores ? doc_scores : reinterpret_cast<float*>(base);
+  char* rest = base + align256((size_t)n_layers * B * n_docs * sizeof(float));
+  hipStream_t s = as_stream(stream);
+  hipError_t e =
+      msa::launch_route_scores(n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs, 0, scores, s);
+  if (e != hipSuccess) return hip_status(e, "msa_route_topk_noalloc (scores)");
+  e = msa::launch_topk((int64_t)n_layers * B, scores, n_docs, k, topk_ids, topk_scores, rest, s);
+  if (e != hipSuccess) return hip_status(e, "msa_route_topk_noalloc (top-k)");
   return MSA_OK;
 }
 

@@ -42,6 +42,8 @@ _SIGS = {
     "msa_topk_docs": ([_I32, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "msa_route_topk_workspace_size": ([_I32, _I32, _I32, _I32], _SZ),
     "msa_route_topk": ([_I32, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "msa_route_topk_noalloc_max_scratch": ([], _SZ),
+    "msa_route_topk_noalloc": ([_I32, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I32, _P, _P, _P, _P], ctypes.c_int),
     "msa_gather_ctx": ([_I32, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _I64, _I32, _P, _P, _P, _P], ctypes.c_int),
     "msa_sparse_decode_workspace_size": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_decode": ([_I32, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _F32, _P, _P, _SZ, _P],
@@ -213,6 +215,21 @@ def msa_route_topk(qr, krbar_route, n_blk, blk_doc, n_docs, k, topk_ids, topk_sc
         _ptr(topk_ids, _I32T, "topk_ids"), _ptr(topk_scores, _F32T, "topk_scores", allow_none=True),
         _ptr(doc_scores, _F32T, "doc_scores", allow_none=True), _ptr(workspace, _ANY, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def msa_route_topk_noalloc_max_scratch() -> int:
+    return int(lib().msa_route_topk_noalloc_max_scratch())
+
+
+def msa_route_topk_noalloc(qr, krbar_route, n_blk, blk_doc, n_docs, k, topk_ids, topk_scores, doc_scores=None,
+                           stream=None, krbar_norm=None):
+    """msa_route_topk without a workspace: the library's fixed per-GPU scratch is used."""
+    L, B, T = qr.shape[0], qr.shape[1], qr.shape[2]
+    _check("msa_route_topk_noalloc", lib().msa_route_topk_noalloc(
+        L, _ptr(qr, _BF16, "qr"), B, T, _ptr(krbar_route, _BF16, "krbar_route"),
+        _norms(krbar_norm, L, n_blk), n_blk, _ptr(blk_doc, _I32T, "blk_doc"), n_docs, k,
+        _ptr(topk_ids, _I32T, "topk_ids"), _ptr(topk_scores, _F32T, "topk_scores", allow_none=True),
+        _ptr(doc_scores, _F32T, "doc_scores", allow_none=True), _stream(stream)))
 
 
 def msa_gather_ctx(topk_ids, doc_blk_off, max_doc_blocks, kbar, vbar, ctx_k, ctx_v, ctx_len, stream=None):

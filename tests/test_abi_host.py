@@ -117,3 +117,22 @@ def test_invalid_arguments_are_rejected_on_the_host(msa):
                                  fake, fake, need - 1, None) == 4
     assert b"workspace" in lib.msa_last_error()
     assert lib.msa_status_string(4) == b"workspace too small"
+
+
+def test_noalloc_route_topk_rejects_oversized_scratch_on_the_host(msa):
+    """The no-allocation entry point refuses work whose scratch exceeds its fixed array, and
+    checks its arguments, before any device call."""
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: validation fails first
+    lib = msa.lib()
+    cap = lib.msa_route_topk_noalloc_max_scratch()
+    assert cap == 64 << 20
+    # 18 layers x 8 queries x 100,000 documents fit; 20M documents of one query do not
+    assert lib.msa_route_topk_workspace_size(18, 8, 100000, 16) <= cap
+    assert lib.msa_route_topk_workspace_size(1, 1, 20000000, 16) > cap
+    assert lib.msa_route_topk_noalloc(1, fake, 1, 64, fake, None, 1000, fake, 20000000, 16, fake, None, None,
+                                      None) == 4
+    assert b"64" in lib.msa_last_error() or b"maximum" in lib.msa_last_error()
+    assert lib.msa_route_topk_noalloc(1, None, 1, 64, fake, None, 1000, fake, 100, 16, fake, None, None, None) == 1
+    assert lib.msa_route_topk_noalloc(1, fake, 1, 64, fake, None, 1000, fake, 10, 16, fake, None, None, None) == 2
+    assert lib.msa_route_topk_noalloc(1, fake, 1, 64, fake, None, 1000, fake, 1000, 300, fake, None, None, None) == 3
