@@ -48,6 +48,13 @@ SCAN_TRAFFIC_BYTES = 57.793e9
 SCAN_TRAFFIC_SOURCE_DIGEST = "5567da15dc0d7ed86687c8d4dca7a95d187fbb4349d7d9acfd3328abc53a65a9"
 
 
+# HBM traffic of one pooling launch over the 1M-token set (18 layers x 947,395 tokens), FETCH_SIZE
+# + WRITE_SIZE passes scaled by the 1 GiB calibration copy, recorded in profiles/pool_1m_tokens.md;
+# valid for the kernel source it was measured on only (null otherwise).
+POOL_TRAFFIC_BYTES = 106.53e9
+POOL_TRAFFIC_SOURCE_DIGEST = "30cadea8d4cfe88b668fedaf833a4129c613dbd9244ee42889f2fd01d3301243"
+
+
 # HBM traffic of one encode launch (18 layers, 1M-token document set), FETCH_SIZE + WRITE_SIZE
 # passes scaled by the 1 GiB calibration copy, recorded in profiles/encode_1m_tokens.md; valid for
 # the kernel source it was measured on only.
@@ -344,6 +351,17 @@ def main():
         pool_ms = float(seg_mean[0])
         result["pooled_tokens_per_s"] = round(L * n_tok / (pool_ms * 1e-3), 1)
         result["pool_GBps"] = round(L * n_tok * POOL_BYTES_PER_TOKEN / (pool_ms * 1e-3) / 1e9, 2)
+        # the pooling dominates a per-token step: it is the line's roofline kernel
+        pool_bytes = L * n_tok * POOL_BYTES_PER_TOKEN + 3 * L * n_blk * 2048 + L * tiles * 16 * 8 * 4
+        pool_gbps = pool_bytes / (pool_ms * 1e-3) / 1e9
+        pool_traffic = (round(POOL_TRAFFIC_BYTES / 1e9, 3)
+                        if (POOL_TRAFFIC_BYTES and cfg.name == "1m"
+                            and source_digest(("pool.hip", "msa_device.hpp")) == POOL_TRAFFIC_SOURCE_DIGEST)
+                        else None)
+        result["roofline"] = {"bound": "hbm", "kernel": "pool_kernel (msa_pool_blocks)", "achieved": round(pool_gbps, 2),
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(pool_gbps / HBM_PEAK_GBPS, 4),
+                              "traffic": pool_traffic, "traffic_unit": "GB per launch",
+                              "algorithmic_GB_per_launch": round(pool_bytes / 1e9, 3)}
 
     # Every step of the path against its own bound (mean over the timed steps).
     def hbm_row(ms, nbytes, note):
@@ -352,8 +370,9 @@ def main():
                 "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes": note}
     rows = {}
     if cfg.per_token:
-        rows["A1_pool"] = hbm_row(float(seg_mean[0]), L * n_tok * POOL_BYTES_PER_TOKEN + 3 * L * n_blk * 2048,
-                                  "K, V, Kr token rows read + K-bar, V-bar, Kr-bar rows written")
+        rows["A1_pool"] = hbm_row(float(seg_mean[0]), L * n_tok * POOL_BYTES_PER_TOKEN + 3 * L * n_blk * 2048
+                                  + L * tiles * 16 * 8 * 4,
+                                  "K, V, Kr token rows read + K-bar, V-bar, Kr-bar rows and Kr-bar norms written")
     LLC_BYTES = 256e6                     # MI355X last-level (Infinity) cache
     scan_bytes = L * n_blk * SCAN_BYTES_PER_BLOCK_LAYER
     if cfg.per_token:
