@@ -15,20 +15,33 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "msa_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+_LIB_PLAIN = os.path.join(_HERE, "liboracle.so")
+# MSA_SANITIZED=1 selects the AddressSanitizer + UndefinedBehaviorSanitizer build (clang, so that one
+# ASan runtime serves the whole process; run Python with that runtime preloaded)
+_SAN = os.environ.get("MSA_SANITIZED") == "1"
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+_LIB = _LIB_SAN if _SAN else _LIB_PLAIN
 
 H, D, BLOCK = 8, 128, 64
 ROW = H * D
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (plain C99, fp64, no FMA contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
-                               "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (plain C99, fp64, no FMA contraction); with sanitize=True a
+    second library, liboracle_san.so, built by clang with -fsanitize=address,undefined."""
+    lib_path = _LIB_SAN if sanitize else _LIB_PLAIN
+    if force or not os.path.exists(lib_path) or os.path.getmtime(lib_path) < os.path.getmtime(_SRC):
+        tmp = lib_path + ".tmp%d" % os.getpid()
+        if sanitize:
+            cmd = ["/opt/rocm/llvm/bin/clang", "-std=c99", "-O1", "-g", "-fno-omit-frame-pointer",
+                   "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-ffp-contract=off",
+                   "-fPIC", "-shared", "-pthread", "-o", tmp, _SRC, "-lm"]
+        else:
+            cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-pthread", "-o", tmp, _SRC,
+                   "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, lib_path)
+    return lib_path
 
 
 _lib = None
@@ -38,7 +51,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
+            build(force=True, sanitize=_SAN)
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double

@@ -14,7 +14,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmsa.so")
+# MSA_SANITIZED=1 loads the build whose host code carries AddressSanitizer and UBSan checks
+LIB_PATH = os.path.join(_PKG, "libmsa_san.so" if os.environ.get("MSA_SANITIZED") == "1" else "libmsa.so")
 
 MSA_OK, MSA_ERR_NULL, MSA_ERR_SHAPE, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(6)
 HEADS, HEAD_DIM, BLOCK_TOKENS, TILE_BLOCKS, MAX_TOPK = 8, 128, 64, 16, 256

@@ -11,7 +11,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "msa.h")
-LIB = os.path.join(ROOT, "routed_kv_memory_amd", "libmsa.so")
+LIB = os.path.join(ROOT, "routed_kv_memory_amd",
+                   "libmsa_san.so" if os.environ.get("MSA_SANITIZED") == "1" else "libmsa.so")
 
 
 @pytest.fixture(scope="module")
