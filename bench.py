@@ -612,6 +612,9 @@ def interleaved_bench(args):
                      "frac": rounds[big]["frac_of_mfma_peak"], "traffic": None},
         "needles_of_query_0_selected": needle_ok,
     }
+    if not args.no_cpu_baseline:
+        # the oracle's scan of layer 0 over every document for query 0's first-round rows, in TFLOP/s
+        result["cpu_baseline"] = cpu_baseline(cfg, di, blk.numpy(), args.cpu_seconds, "TFLOP/s", None, None)
     print(json.dumps(result), flush=True)
 
 
@@ -893,8 +896,8 @@ def cpu_baseline(cfg, di, blk_off, seconds, unit, pool_args, scale):
             dt = time.perf_counter() - t0
             if done >= cfg.B or dt + dt / done > seconds:
                 break
-        work = "routing scan of layer 0, all %d documents (%d blocks), query%s 0..%d (%d tokens each)" % (
-            len(blk_off) - 1, n_blk, "" if done == 1 else "s", done - 1, cfg.T)
+        work = "routing scan of layer 0, all %d documents (%d blocks), %s (%d tokens each)" % (
+            len(blk_off) - 1, n_blk, "query 0" if done == 1 else "queries 0..%d" % (done - 1), cfg.T)
         if unit == "TFLOP/s":
             v = 2.0 * cfg.T * 1024 * n_blk * done / dt / 1e12
         else:
