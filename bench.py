@@ -282,10 +282,14 @@ def main():
     # peak B/s, ~312 flop/B) it is bound by HBM, above it by the matrix cores.
     scan_flop = 2.0 * B * T * 1024 * L * n_blk
     n_chunks = B * ((T + 63) // 64)
-    scan_kernel = ("route_valu_kernel (msa_route_scores)" if T < 16 else
-                   "route_mfma_kernel<%d, %s, %s> (msa_route_scores)"
-                   % (min(4, (T + 15) // 16), "true" if n_chunks == 1 else "false",
-                      "true" if scan_norms is not None else "false"))
+    nt = min(4, (T + 15) // 16)
+    norms_s = "true" if scan_norms is not None else "false"
+    if T < 16:
+        scan_kernel = "route_valu_kernel (msa_route_scores)"
+    elif n_chunks == 1:
+        scan_kernel = "route_mfma_kernel<%d, true, %s> (msa_route_scores)" % (nt, norms_s)
+    else:   # several query chunks: two per workgroup, one head per wave
+        scan_kernel = "route_heads_kernel<%d, %s, 2> (msa_route_scores)" % (nt, norms_s)
     if scan_flop / scan_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
         tflops = scan_flop / (scan_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": scan_kernel,
@@ -607,7 +611,7 @@ def interleaved_bench(args):
                    "rounds_query_tokens": list(cfg.T_rounds), "blocks_per_layer": n_blk, "docs": n_docs, "top_k": k,
                    "route_key_alloc": "one contiguous device allocation" if contiguous else "caching allocator", "scan_key_norms": "read"},
         "rounds": rounds,
-        "roofline": {"bound": "mfma", "kernel": "route_mfma_kernel<4, false, true> (msa_route_scores, round %d)" % (big + 1),
+        "roofline": {"bound": "mfma", "kernel": "route_heads_kernel<4, true, 2> (msa_route_scores, round %d)" % (big + 1),
                      "achieved": rounds[big]["scan_TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": rounds[big]["frac_of_mfma_peak"], "traffic": None},
         "needles_of_query_0_selected": needle_ok,

@@ -26,6 +26,9 @@
 //  * A wave walks the 8 heads of a tile itself, so the head sum, the max over
 //    tokens and the per-document max (a segmented scan keyed by a block ->
 //    document map, each document emitted once) all stay in registers.
+//  * When several query chunks share the key ranges, route_heads_kernel takes two chunks
+//    per workgroup with one head per wave (the query in registers, the head sum through
+//    LDS), halving the key bytes each CU reads per product.
 //  * Queries of < 16 tokens use a vector-ALU kernel over the same layout.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
@@ -402,6 +405,362 @@ route_mfma_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t
   }
 }
 
+// ------------------------------------------------------ many query chunks
+//
+// When several query chunks re-read every key range (B > 1, or more than 64 tokens), the
+// kernel above is bound by how fast a CU's loads come back from L2: every chunk's
+// workgroup reads every key tile, about 64 bytes per clock and CU at full matrix rate,
+// and a CU's L1 sustains about half of that at the L2's latency.  Here a workgroup takes
+// CP = 2 chunks, so each key byte serves 128 tokens.  Each of its 8 waves owns one head:
+// it keeps that head's fragments of both chunks in registers (128 VGPRs) and takes the
+// head's 4 KiB slice of every tile of the range, so the workgroup reads each key byte once
+// per tile and no product touches LDS.  The products are K . Q^T (keys as the A operand),
+// so a lane owns one token column and four blocks: the token's inverse norm is one value
+// per lane, the blocks' norms a 16-byte load.
+//
+// LDS carries only the sum over heads.  Each wave adds its scaled cosines, as fixed-point
+// integers, into one of kSlots tile slots (integer addition, so the sum does not depend on
+// the order in which the waves arrive) and counts itself in the slot's counter one tile
+// later (by then its adds are long complete).  Tile t is folded by wave t mod 8, kFoldLag
+// tiles later: it waits for the count to reach 8, takes the max over tokens, folds the
+// tile's blocks into document maxima, clears the slot and bumps its generation, which the
+// adds of tile t + kSlots wait for.  There is no barrier, and no wait that a slower wave
+// depends on: the slowest wave's slot was folded by a wave ahead of it, and every wave's
+// count of a tile precedes its own next wait.
+//
+// Fixed point: a cosine c in [-1, 1] is held as round(c * 2^21).  fma(x, s, 1.5 * 2^23)
+// with x s = c 2^21 leaves round(c 2^21) in the low mantissa bits of the result (exactly,
+// for |c 2^21| < 2^22), so the bit patterns of the 8 heads' results add, as 32-bit
+// integers, to 8 (1.5 * 2^23 bits) + the sum of the rounded terms.  Each term is off by at
+// most 2^-22, the head mean by at most 2^-22 as well.  Two sums travel as one 64-bit add:
+// the low word's eight biased terms carry exactly 2 into the high word.
+constexpr int kSlots = 8;                         // tile slots of the head sum in LDS
+constexpr int kHRing = 4;                         // tiles of key slices held in registers (one chunk)
+constexpr int kHAhead = 3;                        // tiles in flight beyond the current one
+constexpr int kFoldLag = 3;                       // tiles between a tile's adds and its fold
+constexpr float kFixScale = 2097152.0f;           // 2^21 units per unit of cosine
+constexpr float kFixMagic = 12582912.0f;          // 1.5 * 2^23
+constexpr uint32_t kFixMagicBits = 0x4B400000u;   // its bit pattern
+constexpr float kFixToMean = 1.0f / 16777216.0f;  // 2^-21 per unit, over 8 heads
+
+template <int NT, bool NORMS, int CP>
+__global__ void __launch_bounds__(kScanWG)
+route_heads_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, int32_t n_tc,
+                   const uint4* __restrict__ krt, int64_t tiles, const int32_t* __restrict__ blk_doc,
+                   int32_t n_docs, int32_t L, int32_t R, int32_t exclusive, uint32_t* __restrict__ codes,
+                   const float* __restrict__ knorm) {
+  static_assert(kFoldLag < kHeads && kFoldLag + 2 < kSlots, "a wave folds each tile it owns before its next one");
+  // two chunks' query fragments take 128 VGPRs: then the key ring holds two tiles
+  constexpr int kRingT = CP == 2 ? 2 : kHRing;
+  constexpr int kAheadT = kRingT - 1;
+  __shared__ uint64_t s_sum[kSlots][CP][NT * 2][64];   // head sums of row pairs: [slot][chunk][pair][lane]
+  __shared__ int32_t s_cnt[kSlots];                    // heads added to the slot's tile
+  __shared__ int32_t s_gen[kSlots];                    // tiles of the slot folded so far
+
+  // placement as in route_mfma_kernel: the chunk groups sharing a range sit on one XCD
+  const int C = (n_tc * B);                      // query chunks
+  const int G = (int)(gridDim.x / (unsigned)R);  // groups of CP chunks
+  int r, gidx;
+  {
+    const int i = (int)blockIdx.x;
+    if ((R & 7) == 0) {
+      const int xcd = i & 7, slot = i >> 3;
+      r = xcd + 8 * (slot / G);
+      gidx = slot % G;
+    } else {
+      r = i / G;
+      gidx = i % G;
+    }
+  }
+  // chunk cp of the group; a missing last chunk repeats the group's first and is never folded
+  int cb[CP], ct[CP];
+  bool cvalid[CP];
+#pragma unroll
+  for (int cp = 0; cp < CP; ++cp) {
+    int c = gidx * CP + cp;
+    cvalid[cp] = c < C;
+    if (!cvalid[cp]) c = gidx * CP;
+    cb[cp] = c / n_tc;
+    ct[cp] = (c % n_tc) * kTokChunk;
+  }
+  const int64_t W = (int64_t)L * tiles;
+  const int64_t it_begin = W * r / R;
+  const int64_t it_end = W * (r + 1) / R;
+  if (it_begin >= it_end) return;                // uniform across the workgroup
+
+  const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // this wave's head
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const float ninf = -__builtin_huge_valf();
+
+  for (int i = threadIdx.x; i < kSlots * CP * NT * 2 * 64; i += kScanWG) (&s_sum[0][0][0][0])[i] = 0ull;
+  if (threadIdx.x < kSlots) {
+    s_cnt[threadIdx.x] = 0;
+    s_gen[threadIdx.x] = 0;
+  }
+  __syncthreads();
+
+  // accumulator column of this lane: token 16 nt + j of its chunk
+  bool full_chunk[CP];
+  uint32_t tmask[CP];
+#pragma unroll
+  for (int cp = 0; cp < CP; ++cp) {
+    full_chunk[cp] = ct[cp] + NT * 16 <= T;
+    tmask[cp] = 0;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      if (ct[cp] + nt * 16 + j < T) tmask[cp] |= 1u << nt;
+  }
+  const uint32_t sum_bias = (uint32_t)kHeads * kFixMagicBits;   // modulo 2^32
+
+  int64_t k = 0;   // tiles walked by the workgroup (every wave walks the same sequence)
+  for (int64_t seg = it_begin; seg < it_end;) {
+    const int layer = (int)(seg / tiles);
+    const int64_t layer0 = (int64_t)layer * tiles;
+    const int64_t seg_end = it_end < layer0 + tiles ? it_end : layer0 + tiles;
+    const int n_t = (int)uniform64(seg_end - seg);   // tiles of the segment (< 2^31)
+
+    // head h of each chunk's query as A-operand fragments (rows: tokens 16 nt + j; k: dims
+    // 32 s + 8 g .. + 7) and its inverse norms in fixed-point units, in accumulator order.
+    // s_rq[h] is this wave's own row, and one wave's LDS accesses complete in order.
+    u32x4 qf[CP][4][NT];
+    float rqs[CP][NT];   // token 16 nt + j of chunk cp (the accumulators' column)
+#pragma unroll
+    for (int cp = 0; cp < CP; ++cp) {
+      const uint16_t* qb = qr + (((int64_t)layer * B + cb[cp]) * T) * kRow + h * kDim + g * 8;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int tok = ct[cp] + nt * 16 + j;
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (tok < T) v = *reinterpret_cast<const u32x4*>(qb + (int64_t)tok * kRow + s * 32);
+          qf[cp][s][nt] = v;
+          ss += sumsq8(v);
+        }
+        rqs[cp][nt] = kFixScale / fmaxf(sqrtf(rows4_sum(ss)), kNormEps);
+      }
+    }
+
+    // the ring: per tile this head's four 1 KiB key fragments, the blocks' norms (NORMS)
+    // and their documents; loads are unconditional (past the segment's end the last tile
+    // is fetched again) so that every wait is an exact count.  Wave-uniform addresses
+    // (scalar registers); each lane adds its own offset.
+    const u32x4* src = reinterpret_cast<const u32x4*>(krt + seg * kTileU4 + h * kHeadU4);
+    const float* nsrc = NORMS ? knorm + (seg * kHeads + h) * kTile : nullptr;
+    const int32_t* dsrc = blk_doc + (seg - layer0) * kTile;
+    int issued = 0;
+    u32x4 kb[kRingT][4];
+    float4 nb[kRingT];
+    int32_t db[kRingT];
+    int cnt_slot = -1;      // slot of the tile added but not yet counted
+    bool pend = false;      // a tile this wave is to fold
+    int64_t pend_k = 0;
+    int32_t pend_d = -1;
+    auto issue = [&](int q) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kb[q][s] = src[lane + s * 64];
+      if (NORMS) nb[q] = *reinterpret_cast<const float4*>(nsrc + 4 * g);
+      db[q] = dsrc[j];
+      if (issued + 1 < n_t) {
+        ++issued;
+        src += kTileU4;
+        if (NORMS) nsrc += kHeads * kTile;
+        dsrc += kTile;
+      }
+    };
+#pragma unroll
+    for (int q = 0; q < kAheadT; ++q) {
+      issue(q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Fold of a tile whose head sums are complete, per chunk: the max over the chunk's valid
+    // tokens per block, then the blocks' runs of equal documents into document maxima.
+    // Tiles are folded independently, so a run at either edge of the tile may continue in a
+    // neighbouring tile and is emitted with an atomic max; runs inside are stored directly
+    // when no other workgroup writes this row.
+    auto fold = [&]() {
+      const int slot = (int)(pend_k & (kSlots - 1));
+      while (__builtin_amdgcn_readfirstlane(
+                 __hip_atomic_load(&s_cnt[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != kHeads)
+        __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      // The slot holds, at [cp][2 nt + rp][16 g' + j'], the pair of sums for blocks
+      // 4 g' + 2 rp (low word) and 4 g' + 2 rp + 1 (high word) of token 16 nt + j'.  Lane
+      // (g, jb) takes block jb over tokens 16 nt + 4 g + i (i < 4), reading only its word;
+      // the biased sums stay inside [bias - 2^24, bias + 2^24], so their unsigned max is the
+      // max of the sums (the high word carries 2 more, from the low word).
+      const int jb = lane & 15;
+      const int widx = (((jb >> 1) & 1) * 64 + 16 * (jb >> 2) + 4 * g) * 2 + (jb & 1);   // 32-bit word
+      const uint32_t wbias = sum_bias + (uint32_t)(2 * (jb & 1));
+      uint32_t mxu[CP];
+#pragma unroll
+      for (int cp = 0; cp < CP; ++cp) {
+        const uint32_t* sw = reinterpret_cast<const uint32_t*>(&s_sum[slot][cp][0][0]) + widx;
+        mxu[cp] = 0u;
+        if (full_chunk[cp]) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mxu[cp] = max(mxu[cp], sw[(nt * 2 * 64 + i) * 2]);
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t w = sw[(nt * 2 * 64 + i) * 2];
+              if (ct[cp] + nt * 16 + 4 * g + i < T) mxu[cp] = max(mxu[cp], w);
+            }
+        }
+      }
+      // clear the slot: each lane its own entries (after this wave's reads of them, in order)
+#pragma unroll
+      for (int cp = 0; cp < CP; ++cp)
+#pragma unroll
+        for (int pr = 0; pr < NT * 2; ++pr) s_sum[slot][cp][pr][lane] = 0ull;
+      if (lane == 0) s_cnt[slot] = 0;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0)
+        __hip_atomic_store(&s_gen[slot], (int32_t)(pend_k / kSlots) + 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+      int32_t d = -1;
+      if (lane < kTile) {
+        d = pend_d;
+        if (d >= n_docs) d = -1;   // map entries are trusted only inside [0, n_docs)
+      }
+      const int32_t dprev = row_shr<1>(d, -2);
+      const bool head = lane < kTile && (lane == 0 || dprev != d);
+      const uint64_t heads = __ballot(head);
+      const int hl = 63 - __builtin_clzll(heads);      // head lane of the last run
+#pragma unroll
+      for (int cp = 0; cp < CP; ++cp) {
+        if (!cvalid[cp]) continue;                     // uniform
+        // block jb's max over the chunk's valid tokens (0: none in this lane), as a head mean
+        float v = mxu[cp] != 0u ? (float)(int32_t)(mxu[cp] - wbias) * kFixToMean : ninf;
+        v = rows4_max(v);
+        if (lane >= kTile) v = ninf;
+        {
+          const int ninf_bits = __float_as_int(ninf);
+          float vo = __int_as_float(row_shl<1>(__float_as_int(v), ninf_bits));
+          int32_t dn = row_shl<1>(d, -2);
+          if (dn == d) v = fmaxf(v, vo);
+          vo = __int_as_float(row_shl<2>(__float_as_int(v), ninf_bits));
+          dn = row_shl<2>(d, -2);
+          if (dn == d) v = fmaxf(v, vo);
+          vo = __int_as_float(row_shl<4>(__float_as_int(v), ninf_bits));
+          dn = row_shl<4>(d, -2);
+          if (dn == d) v = fmaxf(v, vo);
+          vo = __int_as_float(row_shl<8>(__float_as_int(v), ninf_bits));
+          dn = row_shl<8>(d, -2);
+          if (dn == d) v = fmaxf(v, vo);
+        }
+        uint32_t* lcodes = codes + ((int64_t)layer * B + cb[cp]) * n_docs;
+        if (head && d >= 0) emit_doc(lcodes, d, v, lane == 0 || lane == hl || !exclusive);
+      }
+    };
+
+    for (int i0 = 0; i0 < n_t; i0 += kRingT) {
+#pragma unroll
+      for (int u = 0; u < kRingT; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue((u + kAheadT) % kRingT);
+        __builtin_amdgcn_sched_barrier(0);
+        const int i = i0 + u;
+        if (i < n_t) {
+          // the slot's generation, read before the products so that its latency hides behind them
+          const int slot = (int)(k & (kSlots - 1));
+          const int32_t gen = (int32_t)(k / kSlots);
+          int32_t gv = __hip_atomic_load(&s_gen[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          // C[block][token] = K . Q^T for head h; lane: token 16 nt + j, blocks 4 g + rr
+          f32x4 acc[CP][NT];
+#pragma unroll
+          for (int cp = 0; cp < CP; ++cp)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[cp][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 kk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, kb[u][s]);
+#pragma unroll
+            for (int cp = 0; cp < CP; ++cp)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt)
+                acc[cp][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, __builtin_bit_cast(bf16x8, qf[cp][s][nt]),
+                                                                      acc[cp][nt], 0, 0, 0);
+            if (!NORMS) kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, kf, kk, 0, 0, 0);
+          }
+          float rk[4];   // 1/max(|k|, eps) of blocks 4 g + rr, head h
+          if (NORMS) {
+            rk[0] = __builtin_amdgcn_rcpf(fmaxf(nb[u].x, kNormEps));
+            rk[1] = __builtin_amdgcn_rcpf(fmaxf(nb[u].y, kNormEps));
+            rk[2] = __builtin_amdgcn_rcpf(fmaxf(nb[u].z, kNormEps));
+            rk[3] = __builtin_amdgcn_rcpf(fmaxf(nb[u].w, kNormEps));
+          } else {
+            // |k_b|^2 is the diagonal entry (b, b) of K K^T: row b = 4 g' + rr' sits in lane
+            // group g' = b >> 2, register rr' = b & 3, column lane j = b
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int src_lane = 16 * g + 4 * g + rr;
+              const float d2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane * 4, __float_as_int(kk[rr])));
+              rk[rr] = __builtin_amdgcn_rsqf(fmaxf(d2, kNormEps * kNormEps));
+            }
+          }
+          // the slot is free once its previous tile (kSlots tiles back) is folded
+          while (__builtin_amdgcn_readfirstlane(gv) != gen) {
+            __builtin_amdgcn_s_sleep(1);
+            gv = __hip_atomic_load(&s_gen[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+          for (int cp = 0; cp < CP; ++cp)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int rp = 0; rp < 2; ++rp) {
+                const uint32_t y0 = __float_as_uint(
+                    __builtin_fmaf(acc[cp][nt][2 * rp], rqs[cp][nt] * rk[2 * rp], kFixMagic));
+                const uint32_t y1 = __float_as_uint(
+                    __builtin_fmaf(acc[cp][nt][2 * rp + 1], rqs[cp][nt] * rk[2 * rp + 1], kFixMagic));
+                __hip_atomic_fetch_add(&s_sum[slot][cp][nt * 2 + rp][lane], (uint64_t)y0 | ((uint64_t)y1 << 32),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              }
+          // count the previous tile in its slot now: its adds have long completed, so the
+          // release finds nothing to wait for (this tile is counted one tile later)
+          if (cnt_slot >= 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            if (lane == 0)
+              __hip_atomic_fetch_add(&s_cnt[cnt_slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+          cnt_slot = slot;
+          if ((int)(k & (kHeads - 1)) == h) {   // this wave folds the tile, kFoldLag tiles from now
+            pend = true;
+            pend_k = k;
+            pend_d = db[u];
+          }
+          ++k;
+          if (pend && k - pend_k > kFoldLag) {
+            fold();
+            pend = false;
+          }
+        }
+      }
+    }
+    if (cnt_slot >= 0) {   // the segment's last tile
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0) __hip_atomic_fetch_add(&s_cnt[cnt_slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      cnt_slot = -1;
+    }
+    if (pend) {     // the segment's last tiles
+      fold();
+      pend = false;
+    }
+    seg = seg_end;
+  }
+}
+
 // ---------------------------------------------------------------- VALU scan
 //
 // One wave per 16-block tile: lane l holds block (l & 15) and, per head, the 8-dim
@@ -483,6 +842,7 @@ constexpr int64_t kMaxRangeTiles = 1024;   // per range when several query chunk
 constexpr int64_t kMinStreamTiles = 512;   // per range when one query chunk streams the keys
 
 int choose_ranges(int C, int cus, int64_t W) {
+  // C: the workgroups that share each range (one per query chunk, or per pair of chunks).
   // R ranges per query chunk; the persistent grid of R*C workgroups (one per CU at a
   // time) should fill whole waves of the device: pick R in [ceil(cus/C), 4*ceil(cus/C)]
   // with the best filled fraction.  When several query chunks share each range, a
@@ -554,23 +914,29 @@ hipError_t launch_route_scores(int32_t L, const uint16_t* qr, int32_t B, int32_t
     if (T >= 16) {
       const int n_tc = (T + kTokChunk - 1) / kTokChunk;
       const int C = B * n_tc;
-      const int R = choose_ranges(C, cus, (int64_t)L * tiles);
+      // one chunk: route_mfma_kernel streams the keys once; several: route_heads_kernel, two
+      // chunks per workgroup (R ranges x G workgroups sharing each range)
+      const bool stream = C == 1;
+      const int G = stream ? 1 : (C + 1) / 2;
+      const int R = choose_ranges(G, cus, (int64_t)L * tiles);
       const int NT = T >= kTokChunk ? 4 : (T + 15) / 16;
-      const dim3 grid((unsigned)(R * C));
+      const dim3 grid((unsigned)(R * G));
       const uint4* kt = reinterpret_cast<const uint4*>(krt);
       const int excl = (n_tc == 1 && !accumulate) ? 1 : 0;
 #define MSA_ROUTE_LAUNCH(NTV, ST, NM)                                                                       \
   hipLaunchKernelGGL((route_mfma_kernel<NTV, ST, NM>), grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, tiles,   \
+                     blk_doc, n_docs, L, R, excl, codes, knorm)
+#define MSA_ROUTE_HEADS(NTV, NM)                                                                       \
+  hipLaunchKernelGGL((route_heads_kernel<NTV, NM, 2>), grid, dim3(kScanWG), 0, s, qr, B, T, n_tc, kt, tiles,  \
                      blk_doc, n_docs, L, R, excl, codes, knorm)
 #define MSA_ROUTE_NT(NTV)                                          \
   if (stream) {                                                    \
     if (knorm) MSA_ROUTE_LAUNCH(NTV, true, true);                  \
     else MSA_ROUTE_LAUNCH(NTV, true, false);                       \
   } else {                                                         \
-    if (knorm) MSA_ROUTE_LAUNCH(NTV, false, true);                 \
-    else MSA_ROUTE_LAUNCH(NTV, false, false);                      \
+    if (knorm) MSA_ROUTE_HEADS(NTV, true);                         \
+    else MSA_ROUTE_HEADS(NTV, false);                              \
   }
-      const bool stream = C == 1;
       switch (NT) {
         case 1: MSA_ROUTE_NT(1); break;
         case 2: MSA_ROUTE_NT(2); break;
@@ -578,6 +944,7 @@ hipError_t launch_route_scores(int32_t L, const uint16_t* qr, int32_t B, int32_t
         default: MSA_ROUTE_NT(4); break;
       }
 #undef MSA_ROUTE_NT
+#undef MSA_ROUTE_HEADS
 #undef MSA_ROUTE_LAUNCH
     } else {
       const dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)B, (unsigned)L);
