@@ -41,10 +41,8 @@ decode_split_kernel(int32_t Hq, const uint16_t* __restrict__ q, const uint16_t* 
   __shared__ uint16_t v_s[kSplitWaves][kWaveRows * kVStride];
   __shared__ float c_m[kSplitWaves][G], c_l[kSplitWaves][G];
 
-  // the 8 KV heads of one split are consecutive workgroups: they read the same rows'
-  // 256-byte head slices at about the same time, so each 2 KiB row is fetched as a unit
-  const int kvh = blockIdx.x % kHeads;
-  const int split = blockIdx.x / kHeads;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
   const int64_t lb = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -267,7 +265,7 @@ hipError_t launch_decode(int32_t L, int32_t B, int32_t Hq, const uint16_t* q, co
   const int64_t parts = (int64_t)L * B * kHeads * n_splits * G;
   float* ws_ml = reinterpret_cast<float*>(ws);
   float* ws_acc = ws_ml + ((2 * parts + 63) / 64) * 64;
-  const dim3 grid((unsigned)(kHeads * n_splits), 1, (unsigned)(L * B));
+  const dim3 grid((unsigned)n_splits, kHeads, (unsigned)(L * B));
   switch (G) {
     case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(64 * kSplitWaves), 0, s, Hq, q, ctx_k, ctx_v, ctx_len, max_ctx,
                                loc_k, loc_v, loc_len, max_loc, scale, n_splits, ws_ml, ws_acc); break;
