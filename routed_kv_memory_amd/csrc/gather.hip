@@ -48,7 +48,7 @@ gather_kernel(int32_t B, const int32_t* __restrict__ ids, int32_t k, const int64
   if (j == 0 && tid == 0) {
     int64_t total = 0;
     for (int i = 0; i < k; ++i) total += s_nb[i];
-    ctx_len[lb] = (int32_t)(total < max_ctx ? total : max_ctx);
+    __builtin_nontemporal_store((int32_t)(total < max_ctx ? total : max_ctx), ctx_len + lb);
   }
   int64_t rows = s_nb[j];
   if (start >= max_ctx) rows = 0;
@@ -60,9 +60,11 @@ gather_kernel(int32_t B, const int32_t* __restrict__ ids, int32_t k, const int64
   uint4* kd = ctx_k + (lb * max_ctx + start) * kRowU4;
   uint4* vd = ctx_v + (lb * max_ctx + start) * kRowU4;
   const int64_t n = rows * kRowU4;
+  // nontemporal stores: the rows go out to memory instead of staying dirty in the caches, where
+  // the decode that reads them next would find them expensive to fetch
   for (int64_t u = tid; u < n; u += kThreads) {
-    kd[u] = ks[u];
-    vd[u] = vs[u];
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(ks + u), reinterpret_cast<u32x4*>(kd + u));
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(vs + u), reinterpret_cast<u32x4*>(vd + u));
   }
 }
 
