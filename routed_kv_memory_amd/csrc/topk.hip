@@ -12,10 +12,10 @@
 // keys, and the next pass merges the candidates until one workgroup per row
 // remains, which writes ids and scores.
 //
-// For k <= 64 a chunk is 2048 keys held in registers (8 per lane): each wave
-// extracts its k best by repeated wave-wide maxima (DPP and row swaps, no LDS),
-// and one wave merges the four waves' lists the same way.  Larger k bitonic-sorts
-// the chunk in LDS.
+// For k <= 64 a chunk is 2048 keys held in registers (8 per lane): each wave finds
+// its k best by ranks among the few keys that can qualify (or, when many keys share a
+// score, by repeated wave-wide maxima), and one wave merges the four waves' lists the
+// same way.  Larger k bitonic-sorts the chunk in LDS.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -139,12 +139,61 @@ __device__ __forceinline__ uint64_t wave_topk(uint64_t (&x)[E], int k, int lane)
   return res;
 }
 
+constexpr int kMaxSurvivors = 128;            // survivors the ranking path takes (else the loop above)
+constexpr int kRankLds = 64 + kMaxSurvivors + 64;   // per wave: lane maxima, survivors, results
+
+// The same selection by ranks, with no chain of k dependent wave-wide maxima.  The k-th
+// largest of the 64 lane maxima is a lower bound T of the k-th largest key (the lanes holding
+// the k largest maxima hold k keys >= T), so only keys >= T can be among the k best; those
+// few survivors are compacted in the wave's LDS area, each survivor's rank is the number of
+// survivors above it (keys are distinct), and the survivor of rank r is the r-th result.  A
+// chunk whose survivors do not fit (many keys of one score) takes wave_topk.  `sm` is the
+// wave's own kRankLds-entry LDS area; one wave's LDS operations complete in order.
+template <int E>
+__device__ __forceinline__ uint64_t wave_topk_rank(uint64_t (&x)[E], int k, int lane, uint64_t* sm) {
+  uint64_t m = x[0];
+#pragma unroll
+  for (int e = 1; e < E; ++e) m = umax64(m, x[e]);
+  sm[lane] = m;
+  int above = 0;
+  for (int l = 0; l < 64; ++l) above += sm[l] > m ? 1 : 0;   // same address in every lane
+  const uint64_t nz = __ballot(m != 0);
+  uint64_t t = 0;                                            // keep every key when < k lanes hold one
+  if (__popcll(nz) >= k) {
+    const uint64_t hit = __ballot(m != 0 && above == k - 1);   // exactly one lane
+    const int src = __ffsll((long long)hit) - 1;
+    t = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(m >> 32), src) << 32) |
+        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, src);
+  }
+  uint64_t* surv = sm + 64;
+  int n_surv = 0;                                            // uniform
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool keep = x[e] != 0 && x[e] >= t;
+    const uint64_t mask = __ballot(keep);
+    const int pos = n_surv + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    if (keep && pos < kMaxSurvivors) surv[pos] = x[e];
+    n_surv += __popcll(mask);
+  }
+  if (n_surv > kMaxSurvivors) return wave_topk(x, k, lane);   // uniform
+  uint64_t* res = sm + 64 + kMaxSurvivors;
+  for (int i = lane; i < n_surv; i += 64) {
+    const uint64_t v = surv[i];
+    int r = 0;
+    for (int q = 0; q < n_surv; ++q) r += surv[q] > v ? 1 : 0;
+    if (r < k) res[r] = v;
+  }
+  return lane < k && lane < n_surv ? res[lane] : 0;
+}
+
 template <bool FROM_SCORES, bool FINAL>
 __global__ void __launch_bounds__(kThreads)
 topk_select_kernel(const float* __restrict__ scores, const uint64_t* __restrict__ keys_in, int64_t n_in,
                    int32_t k, int32_t n_chunks, uint64_t* __restrict__ keys_out, int32_t* __restrict__ ids,
                    float* __restrict__ out_scores) {
   __shared__ uint64_t cand[kThreads / 64][64];
+  __shared__ uint64_t rank_lds[kThreads / 64][kRankLds];
   const int64_t row = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t base = (int64_t)blockIdx.x * kSelChunk + (int64_t)wave * 64 * kSelE + lane;
@@ -159,13 +208,13 @@ topk_select_kernel(const float* __restrict__ scores, const uint64_t* __restrict_
     }
     x[e] = key;
   }
-  cand[wave][lane] = wave_topk(x, k, lane);
+  cand[wave][lane] = wave_topk_rank(x, k, lane, rank_lds[wave]);
   __syncthreads();
   if (wave != 0) return;
   uint64_t y[kThreads / 64];
 #pragma unroll
   for (int w = 0; w < kThreads / 64; ++w) y[w] = cand[w][lane];
-  const uint64_t key = wave_topk(y, k, lane);
+  const uint64_t key = wave_topk_rank(y, k, lane, rank_lds[0]);
   if (lane < k) {
     if (FINAL) {
       ids[row * k + lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
