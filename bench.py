@@ -44,8 +44,8 @@ POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 # WRITE_SIZE rocprofv3 passes (scaled by a 1 GiB calibration kernel) recorded in
 # profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
 # sources' digest differs, the figure is stale and bench.py reports null.
-SCAN_TRAFFIC_BYTES = 57.793e9
-SCAN_TRAFFIC_SOURCE_DIGEST = "5567da15dc0d7ed86687c8d4dca7a95d187fbb4349d7d9acfd3328abc53a65a9"
+SCAN_TRAFFIC_BYTES = 57.790e9
+SCAN_TRAFFIC_SOURCE_DIGEST = "8a462bbdd6aae3c47955a64c3130ea6946cbbc0499908ecd4d5e732e8e78fa0e"
 
 
 # HBM traffic of one pooling launch over the 1M-token set (18 layers x 947,395 tokens), FETCH_SIZE
@@ -58,8 +58,8 @@ POOL_TRAFFIC_SOURCE_DIGEST = "30cadea8d4cfe88b668fedaf833a4129c613dbd9244ee42889
 # HBM traffic of one encode launch (18 layers, 1M-token document set), FETCH_SIZE + WRITE_SIZE
 # passes scaled by the 1 GiB calibration copy, recorded in profiles/encode_1m_tokens.md; valid for
 # the kernel source it was measured on only.
-ENCODE_TRAFFIC_BYTES = 537.0e9
-ENCODE_TRAFFIC_SOURCE_DIGEST = "d3a5447ca4f6a8279b81a57fb83cace06f7218f2083d2d519cfb41dd0c84aa39"
+ENCODE_TRAFFIC_BYTES = 543.1e9
+ENCODE_TRAFFIC_SOURCE_DIGEST = "79853e71207fa062f195069d8f42ae3fea6aea386678cc1d009d7578b15fa291"
 
 
 def source_digest(files=("route.hip", "msa_device.hpp")):

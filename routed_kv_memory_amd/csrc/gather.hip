@@ -10,7 +10,7 @@
 //
 // One workgroup per (selected document, layer, query); block counts of the k
 // selected documents are loaded in parallel and prefix-summed in LDS, then the
-// rows are copied with 16-byte coalesced loads and stores.
+// rows are copied with 16-byte coalesced loads and nontemporal stores.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
