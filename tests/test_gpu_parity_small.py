@@ -194,6 +194,35 @@ def test_topk_chunk_edges(n_docs, k):
             assert np.array_equal(out_h[l, b], ref_sc.astype(np.float32))
 
 
+def test_topk_rank_selection_random_rows():
+    """Rows built so that the k-th best key sits near the lower bound the register path takes
+    from its lanes' maxima (few distinct scores, -inf runs, rows a little longer or shorter than
+    a chunk, k from 1 to 64), and rows with one score repeated so many times that the path keeps
+    its fallback: ids and scores must equal the oracle's full sort exactly."""
+    print("case: top-k rank selection, random rows", flush=True)
+    rng = np.random.default_rng(41)
+    for case in range(12):
+        n_docs = int(rng.choice([33, 511, 2047, 2048, 2049, 4100, 9000]))
+        k = int(rng.integers(1, 65))
+        k = min(k, n_docs)
+        L, B = 1, 3
+        distinct = int(rng.choice([3, 17, 1000]))
+        sc = (rng.integers(0, distinct, (L, B, n_docs)) / distinct).astype(np.float32)
+        sc[0, 1, rng.random(n_docs) < 0.3] = -np.inf
+        sc[0, 2, :] = 0.5
+        sc[0, 2, rng.integers(0, n_docs, 5)] = 0.75
+        ws = torch.empty(max(1, msa.msa_topk_docs_workspace_size(L, B, n_docs, k)), dtype=torch.uint8, device=DEV)
+        ids = torch.empty((L, B, k), dtype=torch.int32, device=DEV)
+        out = torch.empty((L, B, k), dtype=torch.float32, device=DEV)
+        msa.msa_topk_docs(torch.from_numpy(sc).to(DEV), k, ids, out, ws)
+        torch.cuda.synchronize()
+        ids_h, out_h = ids.cpu().numpy(), out.cpu().numpy()
+        for b in range(B):
+            ref_ids, ref_sc = O.topk(sc[0, b].astype(np.float64), k)
+            assert ids_h[0, b].tolist() == ref_ids.tolist(), (case, n_docs, k, b)
+            assert np.array_equal(out_h[0, b], ref_sc.astype(np.float32)), (case, n_docs, k, b)
+
+
 # ----------------------------------------------------------------------- pooling edges
 
 def test_pool_cancellation_tiny_and_huge_values():
