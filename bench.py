@@ -44,15 +44,15 @@ POOL_BYTES_PER_TOKEN = 3 * 1024 * 2       # K, V, Kr rows read
 # WRITE_SIZE rocprofv3 passes (scaled by a 1 GiB calibration kernel) recorded in
 # profiles/route_scan_100m.md.  It describes the kernel source it was measured on only: if the
 # sources' digest differs, the figure is stale and bench.py reports null.
-SCAN_TRAFFIC_BYTES = 57.790e9
-SCAN_TRAFFIC_SOURCE_DIGEST = "8a462bbdd6aae3c47955a64c3130ea6946cbbc0499908ecd4d5e732e8e78fa0e"
+SCAN_TRAFFIC_BYTES = 57.794e9
+SCAN_TRAFFIC_SOURCE_DIGEST = "e330cd7932c352eeecce0daa7e8edeced52e593ed5a80d76be5414330cc46d7c"
 
 
 # HBM traffic of one pooling launch over the 1M-token set (18 layers x 947,395 tokens), FETCH_SIZE
 # + WRITE_SIZE passes scaled by the 1 GiB calibration copy, recorded in profiles/pool_1m_tokens.md;
 # valid for the kernel source it was measured on only (null otherwise).
 POOL_TRAFFIC_BYTES = 106.53e9
-POOL_TRAFFIC_SOURCE_DIGEST = "30cadea8d4cfe88b668fedaf833a4129c613dbd9244ee42889f2fd01d3301243"
+POOL_TRAFFIC_SOURCE_DIGEST = "f2773189c7c7a1c186f1bee1377c6d4288b9582269537870a861b9a39e4a9de8"
 
 
 # HBM traffic of one encode launch (18 layers, 1M-token document set), FETCH_SIZE + WRITE_SIZE
@@ -362,7 +362,10 @@ def main():
                         if (POOL_TRAFFIC_BYTES and cfg.name == "1m"
                             and source_digest(("pool.hip", "msa_device.hpp")) == POOL_TRAFFIC_SOURCE_DIGEST)
                         else None)
-        result["roofline"] = {"bound": "hbm", "kernel": "pool_kernel (msa_pool_blocks)", "achieved": round(pool_gbps, 2),
+        # the library takes 16-wave workgroups when the launch has fewer than 4 per CU
+        pool_w = 16 if 3 * tiles * L < 4 * torch.cuda.get_device_properties(0).multi_processor_count else 4
+        result["roofline"] = {"bound": "hbm", "kernel": "pool_kernel<%d> (msa_pool_blocks)" % pool_w,
+                              "achieved": round(pool_gbps, 2),
                               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(pool_gbps / HBM_PEAK_GBPS, 4),
                               "traffic": pool_traffic, "traffic_unit": "GB per launch",
                               "algorithmic_GB_per_launch": round(pool_bytes / 1e9, 3)}

@@ -8,7 +8,8 @@
 // 方法拆解).
 //
 // One 256-thread workgroup pools one of the three tensors (K, V or Kr) over one 16-block
-// tile of one layer; wave w pools blocks w, w + 4, w + 8 and w + 12 in turn.  Lane l owns
+// tile of one layer; wave w pools blocks w, w + 4, w + 8 and w + 12 in turn (a launch too
+// small to fill the device uses 16 waves, one block each).  Lane l owns
 // 16-byte chunks l and 64 + l of each 2 KiB token row, so a row is two contiguous 1 KiB
 // wave loads (nontemporal: every input byte is read once), eight tokens in flight per
 // step.  Sums are accumulated in fp64: a sum of at most 64 bf16 values is exact there
@@ -97,11 +98,13 @@ __device__ __forceinline__ uint4 mean8(const double* acc, int32_t n, float* ss) 
   return make_uint4(p[0], p[1], p[2], p[3]);
 }
 
-constexpr int kPoolWaves = 4;              // waves per workgroup
-constexpr int kPoolWG = 64 * kPoolWaves;
 constexpr int kU = 8;                      // tokens in flight per wave step
 
-__global__ void __launch_bounds__(kPoolWG) pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
+// W waves per workgroup: 4 (four workgroups share a CU) for large sets; 16 (one block per wave)
+// when the whole launch has too few workgroups to fill the device, where the time is the
+// latency of each wave's sequence of loads rather than bandwidth.
+template <int W>
+__global__ void __launch_bounds__(64 * W) pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                        const uint4* __restrict__ kr, int64_t n_tok,
                                                        const int64_t* __restrict__ tok_off,
                                                        const int64_t* __restrict__ blk_off, int32_t n_docs,
@@ -136,7 +139,7 @@ __global__ void __launch_bounds__(kPoolWG) pool_kernel(const uint4* __restrict__
 
   const int wave = tid >> 6, lane = tid & 63;
   const uint4* src = (tensor == 0 ? k : tensor == 1 ? v : kr) + layer * n_tok * (kRow / 8);
-  for (int b = wave; b < kTile; b += kPoolWaves) {
+  for (int b = wave; b < kTile; b += W) {
     const int64_t blk = tile * kTile + b;
     const int64_t t0 = s_t0[b];
     const int32_t n = s_n[b];
@@ -178,7 +181,7 @@ __global__ void __launch_bounds__(kPoolWG) pool_kernel(const uint4* __restrict__
   uint4* out = tensor == 2 ? krt + (layer * tiles + tile) * (kTileElems / 8)
                            : (tensor == 0 ? kbar : vbar) + (layer * n_blk + tile * kTile) * (kRow / 8);
   const int n_out = tensor == 2 ? kTileElems / 8 : (int)nb * (kRow / 8);
-  for (int i = tid; i < n_out; i += kPoolWG)
+  for (int i = tid; i < n_out; i += 64 * W)
     __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&s_out[i]), reinterpret_cast<u32x4*>(out + i));
 }
 
@@ -212,11 +215,17 @@ hipError_t launch_pool(int32_t L, const uint16_t* k, const uint16_t* v, const ui
                        uint16_t* kbar, uint16_t* vbar, uint16_t* krt, float* krn, hipStream_t s) {
   const int64_t tiles = route_tiles(n_blk);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)(3 * tiles), (unsigned)L), dim3(kPoolWG), 0, s,
-                     reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
-                     reinterpret_cast<const uint4*>(kr), n_tok, doc_tok_off, doc_blk_off, n_docs, n_blk, tiles,
-                     reinterpret_cast<uint4*>(kbar), reinterpret_cast<uint4*>(vbar), reinterpret_cast<uint4*>(krt),
-                     krn);
+  const dim3 grid((unsigned)(3 * tiles), (unsigned)L);
+  if (3 * tiles * (int64_t)L < 4 * (int64_t)stream_cus(s))
+    hipLaunchKernelGGL(pool_kernel<16>, grid, dim3(64 * 16), 0, s, reinterpret_cast<const uint4*>(k),
+                       reinterpret_cast<const uint4*>(v), reinterpret_cast<const uint4*>(kr), n_tok, doc_tok_off,
+                       doc_blk_off, n_docs, n_blk, tiles, reinterpret_cast<uint4*>(kbar), reinterpret_cast<uint4*>(vbar),
+                       reinterpret_cast<uint4*>(krt), krn);
+  else
+    hipLaunchKernelGGL(pool_kernel<4>, grid, dim3(64 * 4), 0, s, reinterpret_cast<const uint4*>(k),
+                       reinterpret_cast<const uint4*>(v), reinterpret_cast<const uint4*>(kr), n_tok, doc_tok_off,
+                       doc_blk_off, n_docs, n_blk, tiles, reinterpret_cast<uint4*>(kbar), reinterpret_cast<uint4*>(vbar),
+                       reinterpret_cast<uint4*>(krt), krn);
   return hipGetLastError();
 }
 

@@ -770,39 +770,58 @@ __global__ void __launch_bounds__(256)
 route_valu_kernel(const uint16_t* __restrict__ qr, int32_t B, int32_t T, const uint4* __restrict__ krt,
                   int64_t n_blk, int64_t tiles,
                   const int32_t* __restrict__ blk_doc, int32_t n_docs, uint32_t* __restrict__ codes) {
+  static_assert(TMAX * kRow / 8 == 8 * 256, "eight 16-byte query chunks per thread");
   __shared__ float q_s[TMAX * kRow];
   __shared__ float rq_s[TMAX * kHeads];
   const int layer = blockIdx.z, b = blockIdx.y;
   const int tid = threadIdx.x;
-  const uint16_t* qbase = qr + (((int64_t)layer * B + b) * T) * kRow;
-  for (int i = tid; i < TMAX * kRow; i += 256) {
-    const int t = i / kRow;
-    q_s[i] = t < T ? __uint_as_float((uint32_t)qbase[i] << 16) : 0.f;
-  }
-  __syncthreads();
-  if (tid < TMAX * kHeads) {
-    const int t = tid / kHeads, h = tid % kHeads;
-    float ss = 0.f;
-    for (int d = 0; d < kDim; ++d) {
-      float a = q_s[t * kRow + h * kDim + d];
-      ss += a * a;
-    }
-    rq_s[tid] = 1.0f / fmaxf(sqrtf(ss), kNormEps);
-  }
-  __syncthreads();
-
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int64_t tile = (int64_t)blockIdx.x * 4 + wave;
+  // this wave's tile: all 8 heads' key fragments requested first (the loads are independent
+  // of the query), clamped to the last tile for waves past the end (never used)
+  const uint4* kt = krt + ((int64_t)layer * tiles + (tile < tiles ? tile : tiles - 1)) * kTileU4;
+  uint4 kw[kHeads][4];
+#pragma unroll
+  for (int h = 0; h < kHeads; ++h)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kw[h][s] = kt[h * kHeadU4 + s * 64 + lane];
+  // the query, 16 bytes per load (chunk i: token i / 128, dims 8 (i % 128) .. + 7), to fp32 in LDS;
+  // the 16 chunks of one (token, head) sit in the 16 lanes of a DPP row, whose sum of squares
+  // gives the head's inverse norm
+  const uint4* qbase = reinterpret_cast<const uint4*>(qr + (((int64_t)layer * B + b) * T) * kRow);
+  uint4 qw[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = tid + 256 * u;
+    qw[u] = i / 128 < T ? qbase[i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = tid + 256 * u;
+    const uint32_t p[4] = {qw[u].x, qw[u].y, qw[u].z, qw[u].w};
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = bf16_lo(p[e]), c = bf16_hi(p[e]);
+      q_s[8 * i + 2 * e] = a;
+      q_s[8 * i + 2 * e + 1] = c;
+      ss += a * a + c * c;
+    }
+    ss = row16_sum(ss);
+    if ((tid & 15) == 0) rq_s[i / 16] = 1.0f / fmaxf(sqrtf(ss), kNormEps);   // (token, head) = i / 16
+  }
+  __syncthreads();
   if (tile >= tiles) return;
-  const uint4* kt = krt + ((int64_t)layer * tiles + tile) * kTileU4;
+
   float sc[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) sc[t] = 0.f;
-  for (int h = 0; h < kHeads; ++h) {
+#pragma unroll
+  for (int h = 0; h < kHeads; ++h) {   // unrolled: kw stays in registers
     float x[32];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint4 w = kt[h * kHeadU4 + s * 64 + lane];
+      const uint4 w = kw[h][s];
       const uint32_t p[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) { x[s * 8 + 2 * e] = bf16_lo(p[e]); x[s * 8 + 2 * e + 1] = bf16_hi(p[e]); }
