@@ -27,6 +27,8 @@
  *    one exception, content K/V in pinned host memory, is noted at msa_gather_ctx); the
  *    library never allocates, frees or keeps them.  Workspaces are caller-owned
  *    device memory of at least the size the matching *_workspace_size returns.
+ *  - bf16 arrays (and the scan's optional key norms, the prefill's output) are moved in
+ *    16-byte vectors: their pointers must be 16-byte aligned, else MSA_ERR_SHAPE.
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls
  *    validate on the host, enqueue kernels on `stream` and return; results are
  *    valid once the stream has been synchronised.  No call synchronises.

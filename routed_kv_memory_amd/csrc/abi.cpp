@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 
 #include "msa_kernels.hpp"
@@ -32,6 +33,14 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The kernels move bf16 rows (and a few fp32 arrays) in 16-byte vectors: such pointers must be
+// 16-byte aligned.  NULL entries (optional arguments) pass.
+bool all_aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) & 15u) return false;
+  return true;
+}
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -134,6 +143,8 @@ MSA_API int msa_pool_blocks(int32_t n_layers, const uint16_t* k, const uint16_t*
                             float* krbar_norm, void* stream) {
   if (!k || !v || !kr || !doc_tok_off || !doc_blk_off || !kbar || !vbar || !krbar_route)
     return fail(MSA_ERR_NULL, "msa_pool_blocks: null pointer");
+  if (!all_aligned16({k, v, kr, kbar, vbar, krbar_route}))
+    return fail(MSA_ERR_SHAPE, "msa_pool_blocks: bf16 arrays must be 16-byte aligned");
   if (n_layers < 1 || n_docs < 1 || n_tok < 0 || n_blk < 0)
     return fail(MSA_ERR_SHAPE, "msa_pool_blocks: n_layers=%d n_docs=%d n_tok=%lld n_blk=%lld", n_layers, n_docs,
                 (long long)n_tok, (long long)n_blk);
@@ -146,6 +157,8 @@ MSA_API int msa_pool_blocks(int32_t n_layers, const uint16_t* k, const uint16_t*
 MSA_API int msa_pack_route_keys(int32_t n_layers, const uint16_t* krbar_rows, int64_t n_blk, uint16_t* krbar_route,
                                 float* krbar_norm, void* stream) {
   if (!krbar_rows || !krbar_route) return fail(MSA_ERR_NULL, "msa_pack_route_keys: null pointer");
+  if (!all_aligned16({krbar_rows, krbar_route}))
+    return fail(MSA_ERR_SHAPE, "msa_pack_route_keys: bf16 arrays must be 16-byte aligned");
   if (n_layers < 1 || n_blk < 0) return fail(MSA_ERR_SHAPE, "msa_pack_route_keys: n_layers=%d n_blk=%lld", n_layers,
                                              (long long)n_blk);
   if (msa::route_tiles(n_blk) > INT32_MAX) return fail(MSA_ERR_UNSUPPORTED, "msa_pack_route_keys: n_blk too large");
@@ -166,8 +179,11 @@ MSA_API int msa_block_doc_map(const int64_t* doc_blk_off, int32_t n_docs, int64_
 }
 
 static int check_route_args(const char* fn, int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
-                            const uint16_t* krbar_route, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs) {
+                            const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
+                            const int32_t* blk_doc, int32_t n_docs) {
   if (!qr || !krbar_route || !blk_doc) return fail(MSA_ERR_NULL, "%s: null pointer", fn);
+  if (!all_aligned16({qr, krbar_route, krbar_norm}))
+    return fail(MSA_ERR_SHAPE, "%s: qr, the route keys and their norms must be 16-byte aligned", fn);
   if (n_layers < 1 || B < 1 || T < 1 || n_docs < 1 || n_blk < 0)
     return fail(MSA_ERR_SHAPE, "%s: n_layers=%d B=%d T=%d n_docs=%d n_blk=%lld", fn, n_layers, B, T, n_docs,
                 (long long)n_blk);
@@ -181,7 +197,7 @@ static int check_route_args(const char* fn, int32_t n_layers, const uint16_t* qr
 MSA_API int msa_route_scores(int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T, const uint16_t* krbar_route,
                              const float* krbar_norm, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs, int32_t accumulate,
                              float* doc_scores, void* stream) {
-  int st = check_route_args("msa_route_scores", n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs);
+  int st = check_route_args("msa_route_scores", n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs);
   if (st) return st;
   if (!doc_scores) return fail(MSA_ERR_NULL, "msa_route_scores: null pointer");
   return hip_status(msa::launch_route_scores(n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs,
@@ -224,7 +240,7 @@ MSA_API int msa_route_topk(int32_t n_layers, const uint16_t* qr, int32_t B, int3
                            const float* krbar_norm, int64_t n_blk, const int32_t* blk_doc, int32_t n_docs, int32_t k, int32_t* topk_ids,
                            float* topk_scores, float* doc_scores, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  int st = check_route_args("msa_route_topk", n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs);
+  int st = check_route_args("msa_route_topk", n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc, n_docs);
   if (st) return st;
   if (!topk_ids || !workspace) return fail(MSA_ERR_NULL, "msa_route_topk: null pointer");
   if (k < 1 || k > n_docs) return fail(MSA_ERR_SHAPE, "msa_route_topk: k=%d n_docs=%d", k, n_docs);
@@ -289,7 +305,8 @@ MSA_API int msa_route_topk_noalloc(int32_t n_layers, const uint16_t* qr, int32_t
                                    const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
                                    const int32_t* blk_doc, int32_t n_docs, int32_t k, int32_t* topk_ids,
                                    float* topk_scores, float* doc_scores, void* stream) {
-  int st = check_route_args("msa_route_topk_noalloc", n_layers, qr, B, T, krbar_route, n_blk, blk_doc, n_docs);
+  int st = check_route_args("msa_route_topk_noalloc", n_layers, qr, B, T, krbar_route, krbar_norm, n_blk, blk_doc,
+                            n_docs);
   if (st) return st;
   if (!topk_ids) return fail(MSA_ERR_NULL, "msa_route_topk_noalloc: null pointer");
   if (k < 1 || k > n_docs) return fail(MSA_ERR_SHAPE, "msa_route_topk_noalloc: k=%d n_docs=%d", k, n_docs);
@@ -324,6 +341,8 @@ MSA_API int msa_gather_ctx(int32_t n_layers, int32_t B, const int32_t* topk_ids,
                            int32_t* ctx_len, void* stream) {
   if (!topk_ids || !doc_blk_off || !kbar || !vbar || !ctx_k || !ctx_v || !ctx_len)
     return fail(MSA_ERR_NULL, "msa_gather_ctx: null pointer");
+  if (!all_aligned16({kbar, vbar, ctx_k, ctx_v}))
+    return fail(MSA_ERR_SHAPE, "msa_gather_ctx: bf16 arrays must be 16-byte aligned");
   if (n_layers < 1 || B < 1 || k < 1 || n_docs < 1 || max_doc_blocks < 0 || n_blk < 0 || max_ctx < 1)
     return fail(MSA_ERR_SHAPE, "msa_gather_ctx: n_layers=%d B=%d k=%d n_docs=%d max_doc_blocks=%d max_ctx=%d",
                 n_layers, B, k, n_docs, max_doc_blocks, max_ctx);
@@ -355,6 +374,8 @@ MSA_API int msa_sparse_decode(int32_t n_layers, int32_t B, int32_t Hq, const uin
                               void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !ctx_k || !ctx_v || !ctx_len || !out || !workspace) return fail(MSA_ERR_NULL, "msa_sparse_decode: null pointer");
   if (max_loc > 0 && (!loc_k || !loc_v || !loc_len)) return fail(MSA_ERR_NULL, "msa_sparse_decode: null local KV");
+  if (!all_aligned16({q, ctx_k, ctx_v, max_loc > 0 ? loc_k : nullptr, max_loc > 0 ? loc_v : nullptr}))
+    return fail(MSA_ERR_SHAPE, "msa_sparse_decode: bf16 arrays must be 16-byte aligned");
   if (n_layers < 1 || B < 1 || Hq < 1 || max_ctx < 1 || max_loc < 0 || Hq % MSA_HEADS != 0)
     return fail(MSA_ERR_SHAPE, "msa_sparse_decode: n_layers=%d B=%d Hq=%d max_ctx=%d max_loc=%d", n_layers, B, Hq,
                 max_ctx, max_loc);
@@ -376,6 +397,8 @@ MSA_API int msa_encode_blocks(int32_t n_layers, int32_t H, const uint16_t* x, in
                               uint16_t* kbar, uint16_t* vbar, uint16_t* krbar_route, float* krbar_norm, void* stream) {
   if (!x || !w_k || !w_v || !w_kr || !w_norm || !doc_tok_off || !doc_blk_off || !kbar || !vbar || !krbar_route)
     return fail(MSA_ERR_NULL, "msa_encode_blocks: null pointer");
+  if (!all_aligned16({x, w_k, w_v, w_kr}))
+    return fail(MSA_ERR_SHAPE, "msa_encode_blocks: hidden rows and weights must be 16-byte aligned");
   if (n_layers < 1 || H < 128 || H % 128 != 0 || n_tok < 1 || n_docs < 1 || n_blk < 0 || !(eps >= 0.f) ||
       !(theta > 0.f))
     return fail(MSA_ERR_SHAPE, "msa_encode_blocks: n_layers=%d H=%d n_tok=%lld n_docs=%d n_blk=%lld", n_layers, H,
@@ -393,6 +416,8 @@ MSA_API int msa_sparse_prefill(int32_t n_layers, int32_t B, int32_t T, int32_t H
                                float scale, float* out, void* stream) {
   if (!q || !ctx_k || !ctx_v || !ctx_len || !loc_k || !loc_v || !loc_len || !out)
     return fail(MSA_ERR_NULL, "msa_sparse_prefill: null pointer");
+  if (!all_aligned16({q, ctx_k, ctx_v, loc_k, loc_v, out}))
+    return fail(MSA_ERR_SHAPE, "msa_sparse_prefill: q, K/V and out must be 16-byte aligned");
   if (n_layers < 1 || B < 1 || T < 1 || Hq < 1 || max_ctx < 1 || max_loc < T || Hq % MSA_HEADS != 0)
     return fail(MSA_ERR_SHAPE, "msa_sparse_prefill: n_layers=%d B=%d T=%d Hq=%d max_ctx=%d max_loc=%d", n_layers,
                 B, T, Hq, max_ctx, max_loc);

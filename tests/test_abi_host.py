@@ -109,6 +109,22 @@ def test_invalid_arguments_are_rejected_on_the_host(msa):
                                  fake, fake, None, None) == 2
     assert lib.msa_encode_blocks(1, 128, fake, 10, fake, fake, fake, fake, F(1e-6), F(0.0), fake, fake, 1, 1, fake,
                                  fake, fake, None, None) == 2
+    # bf16 arrays not 16-byte aligned (each otherwise valid call)
+    odd = P(0x1002)
+    assert lib.msa_pool_blocks(1, fake, odd, fake, 10, fake, fake, 1, 1, fake, fake, fake, fake, None) == 2
+    assert b"aligned" in lib.msa_last_error()
+    assert lib.msa_pack_route_keys(1, odd, 16, fake, None, None) == 2
+    assert lib.msa_route_scores(1, odd, 1, 8, fake, None, 16, fake, 1, 0, fake, None) == 2
+    assert lib.msa_route_scores(1, fake, 1, 64, fake, P(0x1004), 16, fake, 1, 0, fake, None) == 2   # key norms
+    assert lib.msa_route_topk(1, fake, 1, 8, odd, None, 16, fake, 4, 2, fake, None, None, fake, 1 << 20, None) == 2
+    assert lib.msa_gather_ctx(1, 1, fake, 4, fake, 10, 8, fake, fake, 100, 32, odd, fake, fake, None) == 2
+    assert lib.msa_sparse_decode(1, 1, 32, fake, fake, fake, fake, 16, fake, odd, fake, 4, ctypes.c_float(0.1),
+                                 fake, fake, 1 << 20, None) == 2
+    assert lib.msa_sparse_prefill(1, 1, 4, 32, fake, fake, fake, fake, 8, fake, fake, fake, 4, ctypes.c_float(0.1),
+                                  P(0x1008), None) == 2
+    F = ctypes.c_float
+    assert lib.msa_encode_blocks(1, 128, fake, 10, fake, odd, fake, fake, F(1e-6), F(1e6), fake, fake, 1, 1, fake,
+                                 fake, fake, None, None) == 2
     # workspace too small
     need = lib.msa_route_topk_workspace_size(2, 1, 100000, 16)
     assert lib.msa_route_topk(2, fake, 1, 8, fake, None, 1000, fake, 100000, 16, fake, None, None, fake, need - 1,
