@@ -18,6 +18,7 @@ namespace msa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kCopyBatch = 8;   // 16-byte pieces of K and of V in flight per thread
 
 __global__ void __launch_bounds__(kThreads)
 gather_kernel(int32_t B, const int32_t* __restrict__ ids, int32_t k, const int64_t* __restrict__ off,
@@ -60,11 +61,28 @@ gather_kernel(int32_t B, const int32_t* __restrict__ ids, int32_t k, const int64
   uint4* kd = ctx_k + (lb * max_ctx + start) * kRowU4;
   uint4* vd = ctx_v + (lb * max_ctx + start) * kRowU4;
   const int64_t n = rows * kRowU4;
-  // nontemporal stores: the rows go out to memory instead of staying dirty in the caches, where
-  // the decode that reads them next would find them expensive to fetch
-  for (int64_t u = tid; u < n; u += kThreads) {
-    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(ks + u), reinterpret_cast<u32x4*>(kd + u));
-    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(vs + u), reinterpret_cast<u32x4*>(vd + u));
+  // kCopyBatch 16-byte pieces of K and of V per thread in flight at once (a document's rows are a
+  // few tens of KiB: one or two rounds of loads instead of one round per 4 KiB); nontemporal
+  // stores: the rows go out to memory instead of staying dirty in the caches, where the decode
+  // that reads them next would find them expensive to fetch
+  for (int64_t u0 = tid; u0 < n; u0 += (int64_t)kCopyBatch * kThreads) {
+    u32x4 a[kCopyBatch], b[kCopyBatch];
+#pragma unroll
+    for (int e = 0; e < kCopyBatch; ++e) {
+      const int64_t u = u0 + (int64_t)e * kThreads;
+      if (u < n) {
+        a[e] = *reinterpret_cast<const u32x4*>(ks + u);
+        b[e] = *reinterpret_cast<const u32x4*>(vs + u);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kCopyBatch; ++e) {
+      const int64_t u = u0 + (int64_t)e * kThreads;
+      if (u < n) {
+        __builtin_nontemporal_store(a[e], reinterpret_cast<u32x4*>(kd + u));
+        __builtin_nontemporal_store(b[e], reinterpret_cast<u32x4*>(vd + u));
+      }
+    }
   }
 }
 
