@@ -362,9 +362,9 @@ def main():
                         if (POOL_TRAFFIC_BYTES and cfg.name == "1m"
                             and source_digest(("pool.hip", "msa_device.hpp")) == POOL_TRAFFIC_SOURCE_DIGEST)
                         else None)
-        # the library takes 16-wave workgroups when the launch has fewer than 4 per CU
-        pool_w = 16 if 3 * tiles * L < 4 * torch.cuda.get_device_properties(0).multi_processor_count else 4
-        result["roofline"] = {"bound": "hbm", "kernel": "pool_kernel<%d> (msa_pool_blocks)" % pool_w,
+        # the library takes one tile per workgroup when the launch would have fewer than 4 per CU
+        small = 3 * tiles * L < 4 * torch.cuda.get_device_properties(0).multi_processor_count
+        result["roofline"] = {"bound": "hbm", "kernel": "pool_kernel<16, %d> (msa_pool_blocks)" % (1 if small else 4),
                               "achieved": round(pool_gbps, 2),
                               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(pool_gbps / HBM_PEAK_GBPS, 4),
                               "traffic": pool_traffic, "traffic_unit": "GB per launch",

@@ -7,24 +7,23 @@
 // "【MSA】突破100M Token 上下文…", 3.3.2; xiaohongrsx.github.io "MSA paper reading",
 // 方法拆解).
 //
-// One 256-thread workgroup pools one of the three tensors (K, V or Kr) over one 16-block
-// tile of one layer; wave w pools blocks w, w + 4, w + 8 and w + 12 in turn (a launch too
-// small to fill the device uses 16 waves, one block each).  Lane l owns
-// 16-byte chunks l and 64 + l of each 2 KiB token row, so a row is two contiguous 1 KiB
-// wave loads (nontemporal: every input byte is read once), eight tokens in flight per
-// step.  Sums are accumulated in fp64: a sum of at most 64 bf16 values is exact there
-// unless their magnitudes span more than 2^39, so the mean is the exactly rounded fp64
-// quotient, rounded once more to bf16 (nearest-even) straight from fp64.  The tile's 16
-// output rows (row-major for K-bar and V-bar, the route layout for the routing keys) are
-// staged in LDS and written at the end as one contiguous 32 KiB run with nontemporal
-// stores.  Small register and LDS footprints (32 KiB per workgroup) let four workgroups
-// share a CU, so 16 waves keep loads in flight.
+// One 1024-thread workgroup (16 waves, the whole CU) pools one of the three tensors (K, V or
+// Kr) over four consecutive 16-block tiles of one layer; wave w pools blocks w, w + 16, w + 32
+// and w + 48 in turn (a launch too small to fill the device takes one tile per workgroup, one
+// block per wave).  Lane l owns 16-byte chunks l and 64 + l of each 2 KiB token row, so a row
+// is two contiguous 1 KiB wave loads (nontemporal: every input byte is read once), eight tokens
+// in flight per step.  Sums are accumulated in fp64: a sum of at most 64 bf16 values is exact
+// there unless their magnitudes span more than 2^39, so the mean is the exactly rounded fp64
+// quotient, rounded once more to bf16 (nearest-even) straight from fp64.  The tiles' 64 output
+// rows (row-major for K-bar and V-bar, the route layout for the routing keys) are staged in LDS
+// (128 KiB) and written at the end as one contiguous 128 KiB run with nontemporal stores.
 //
-// Writes are 1.6% of the bytes but set the pace: measured on the 1M-token set, the same
-// kernel streams its reads at 0.855 of peak HBM bandwidth with the writes left out, 0.697
-// with ordinary stores issued as each block finishes, and 0.770 with the staged runs and
-// nontemporal stores (reads and writes share the HBM bus, and every change of direction
-// costs time).
+// Writes are 1.6% of the bytes but set the pace, and the size of the runs they arrive in
+// decides their cost in HBM: on 4 layers of the 1M-token set (22.9 GB per launch) the same
+// pooling ran at 0.750 of peak HBM bandwidth with 32 KiB runs (one tile per 256-thread
+// workgroup, four per CU), 0.779 with 64 KiB runs (two tiles, 8 waves), 0.823 with 128 KiB runs
+// (this layout), and 0.861 with the stores absorbed by the caches (every workgroup writing the
+// same 32 KiB, a timing copy).  Ordinary stores issued block by block ran at 0.697.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -100,10 +99,11 @@ __device__ __forceinline__ uint4 mean8(const double* acc, int32_t n, float* ss) 
 
 constexpr int kU = 8;                      // tokens in flight per wave step
 
-// W waves per workgroup: 4 (four workgroups share a CU) for large sets; 16 (one block per wave)
-// when the whole launch has too few workgroups to fill the device, where the time is the
-// latency of each wave's sequence of loads rather than bandwidth.
-template <int W>
+// W waves per workgroup over TPW consecutive 16-block tiles of one tensor and layer, each wave
+// pooling blocks wave, wave + W, ...: <16, 4> for large sets (one workgroup per CU, its 128 KiB of
+// outputs written as one run), <16, 1> when the launch has too few workgroups to fill the device
+// (one block per wave: the time is each wave's chain of loads, not bandwidth).
+template <int W, int TPW>
 __global__ void __launch_bounds__(64 * W) pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                        const uint4* __restrict__ kr, int64_t n_tok,
                                                        const int64_t* __restrict__ tok_off,
@@ -111,15 +111,16 @@ __global__ void __launch_bounds__(64 * W) pool_kernel(const uint4* __restrict__ 
                                                        int64_t n_blk, int64_t tiles, uint4* __restrict__ kbar,
                                                        uint4* __restrict__ vbar, uint4* __restrict__ krt,
                                                        float* __restrict__ krn) {
-  __shared__ int64_t s_t0[kTile];
-  __shared__ int32_t s_n[kTile];
-  __shared__ uint4 s_out[kTileElems / 8];     // the tile's 16 pooled rows (route layout for Kr)
+  constexpr int NB = kTile * TPW;             // blocks of the workgroup
+  __shared__ int64_t s_t0[NB];
+  __shared__ int32_t s_n[NB];
+  __shared__ uint4 s_out[TPW * (kTileElems / 8)];   // the tiles' pooled rows (route layout for Kr)
   const int tensor = (int)(blockIdx.x % 3u);  // 0: K, 1: V, 2: Kr (uniform per workgroup)
-  const int64_t tile = blockIdx.x / 3u;
+  const int64_t tile0 = (int64_t)(blockIdx.x / 3u) * TPW;
   const int64_t layer = blockIdx.y;
   const int tid = threadIdx.x;
-  if (tid < kTile) {
-    int64_t blk = tile * kTile + tid;
+  if (tid < NB) {
+    int64_t blk = tile0 * kTile + tid;
     int64_t t0 = 0;
     int32_t n = 0;
     if (blk < n_blk) {
@@ -139,8 +140,7 @@ __global__ void __launch_bounds__(64 * W) pool_kernel(const uint4* __restrict__ 
 
   const int wave = tid >> 6, lane = tid & 63;
   const uint4* src = (tensor == 0 ? k : tensor == 1 ? v : kr) + layer * n_tok * (kRow / 8);
-  for (int b = wave; b < kTile; b += W) {
-    const int64_t blk = tile * kTile + b;
+  for (int b = wave; b < NB; b += W) {
     const int64_t t0 = s_t0[b];
     const int32_t n = s_n[b];
     double acc[2][8] = {};
@@ -159,6 +159,7 @@ __global__ void __launch_bounds__(64 * W) pool_kernel(const uint4* __restrict__ 
     for (; t < n; ++t)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) add8(acc[hh], ld_nt(src + (t0 + t) * (kRow / 8) + hh * 64 + lane));
+    const int tl = b / kTile, bl = b % kTile;   // tile of the workgroup, block of the tile
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int c16 = hh * 64 + lane;   // chunk of the row: head c16 / 16, dims (c16 % 16) * 8
@@ -169,18 +170,19 @@ __global__ void __launch_bounds__(64 * W) pool_kernel(const uint4* __restrict__ 
         s_out[b * (kRow / 8) + c16] = o;
       } else {
         const int h = c16 >> 4, c = c16 & 15;
-        s_out[h * (kTile * 16) + c * kTile + b] = o;     // route layout: [h][c][b][8]
+        s_out[tl * (kTileElems / 8) + h * (kTile * 16) + c * kTile + bl] = o;   // route layout: [h][c][b][8]
         ss = row16_sum(ss);   // the 16 lanes of a DPP row hold the 16 chunks of head h
-        if (krn && c == 0) krn[((layer * tiles + tile) * kHeads + h) * kTile + b] = sqrtf(ss);
+        if (krn && c == 0 && tile0 + tl < tiles) krn[((layer * tiles + tile0 + tl) * kHeads + h) * kTile + bl] = sqrtf(ss);
       }
     }
   }
   __syncthreads();
-  // one contiguous run per tile: the real blocks' rows of K-bar / V-bar, the whole route tile
-  const int64_t nb = n_blk - tile * kTile < kTile ? n_blk - tile * kTile : kTile;
-  uint4* out = tensor == 2 ? krt + (layer * tiles + tile) * (kTileElems / 8)
-                           : (tensor == 0 ? kbar : vbar) + (layer * n_blk + tile * kTile) * (kRow / 8);
-  const int n_out = tensor == 2 ? kTileElems / 8 : (int)nb * (kRow / 8);
+  // one contiguous run: the real blocks' rows of K-bar / V-bar, the whole route tiles
+  const int64_t nt = tiles - tile0 < TPW ? tiles - tile0 : TPW;
+  const int64_t nb = n_blk - tile0 * kTile < NB ? n_blk - tile0 * kTile : NB;
+  uint4* out = tensor == 2 ? krt + (layer * tiles + tile0) * (kTileElems / 8)
+                           : (tensor == 0 ? kbar : vbar) + (layer * n_blk + tile0 * kTile) * (kRow / 8);
+  const int n_out = tensor == 2 ? (int)nt * (kTileElems / 8) : (int)nb * (kRow / 8);
   for (int i = tid; i < n_out; i += 64 * W)
     __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&s_out[i]), reinterpret_cast<u32x4*>(out + i));
 }
@@ -215,17 +217,19 @@ hipError_t launch_pool(int32_t L, const uint16_t* k, const uint16_t* v, const ui
                        uint16_t* kbar, uint16_t* vbar, uint16_t* krt, float* krn, hipStream_t s) {
   const int64_t tiles = route_tiles(n_blk);
   if (tiles == 0) return hipSuccess;
-  const dim3 grid((unsigned)(3 * tiles), (unsigned)L);
-  if (3 * tiles * (int64_t)L < 4 * (int64_t)stream_cus(s))
-    hipLaunchKernelGGL(pool_kernel<16>, grid, dim3(64 * 16), 0, s, reinterpret_cast<const uint4*>(k),
-                       reinterpret_cast<const uint4*>(v), reinterpret_cast<const uint4*>(kr), n_tok, doc_tok_off,
-                       doc_blk_off, n_docs, n_blk, tiles, reinterpret_cast<uint4*>(kbar), reinterpret_cast<uint4*>(vbar),
-                       reinterpret_cast<uint4*>(krt), krn);
-  else
-    hipLaunchKernelGGL(pool_kernel<4>, grid, dim3(64 * 4), 0, s, reinterpret_cast<const uint4*>(k),
-                       reinterpret_cast<const uint4*>(v), reinterpret_cast<const uint4*>(kr), n_tok, doc_tok_off,
-                       doc_blk_off, n_docs, n_blk, tiles, reinterpret_cast<uint4*>(kbar), reinterpret_cast<uint4*>(vbar),
-                       reinterpret_cast<uint4*>(krt), krn);
+  if (3 * tiles * (int64_t)L < 4 * (int64_t)stream_cus(s)) {
+    hipLaunchKernelGGL((pool_kernel<16, 1>), dim3((unsigned)(3 * tiles), (unsigned)L), dim3(64 * 16), 0, s,
+                       reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
+                       reinterpret_cast<const uint4*>(kr), n_tok, doc_tok_off, doc_blk_off, n_docs, n_blk, tiles,
+                       reinterpret_cast<uint4*>(kbar), reinterpret_cast<uint4*>(vbar), reinterpret_cast<uint4*>(krt),
+                       krn);
+  } else {
+    hipLaunchKernelGGL((pool_kernel<16, 4>), dim3((unsigned)(3 * ((tiles + 3) / 4)), (unsigned)L), dim3(64 * 16), 0,
+                       s, reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
+                       reinterpret_cast<const uint4*>(kr), n_tok, doc_tok_off, doc_blk_off, n_docs, n_blk, tiles,
+                       reinterpret_cast<uint4*>(kbar), reinterpret_cast<uint4*>(vbar), reinterpret_cast<uint4*>(krt),
+                       krn);
+  }
   return hipGetLastError();
 }
 
