@@ -52,7 +52,7 @@ SCAN_TRAFFIC_SOURCE_DIGEST = "e330cd7932c352eeecce0daa7e8edeced52e593ed5a80d76be
 # + WRITE_SIZE passes scaled by the 1 GiB calibration copy, recorded in profiles/pool_1m_tokens.md;
 # valid for the kernel source it was measured on only (null otherwise).
 POOL_TRAFFIC_BYTES = 106.53e9
-POOL_TRAFFIC_SOURCE_DIGEST = "f2773189c7c7a1c186f1bee1377c6d4288b9582269537870a861b9a39e4a9de8"
+POOL_TRAFFIC_SOURCE_DIGEST = "42db7ac2fdcbc30c564bb556aac3d7e8f15abe76b428b5049b39791270a20d0c"
 
 
 # HBM traffic of one encode launch (18 layers, 1M-token document set), FETCH_SIZE + WRITE_SIZE
