@@ -154,6 +154,8 @@ def parse():
                     help="host-tier: layer groups whose top-k and host gather overlap the next group's scan")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the second timing of the step as one replayed HIP graph (path workloads)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a 1 GiB fill and a 1 GiB elementwise copy (kernels of known traffic, "
                          "used to scale hardware byte counters)")
@@ -267,6 +269,21 @@ def main():
     seg_mean = seg.mean(axis=0)
     ms_step = wall * 1e3 / args.steps
 
+    # The same step recorded once in a HIP graph and replayed K times: the launches' gaps are
+    # what differs.  Reported beside the eager step (value is computed from the eager step).
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
     # sanity of the result (cheap, outside the timed region): planted needles are the top-k
     nd = S.needle_docs(cfg)
     ids_h = ids.cpu().numpy()
@@ -321,6 +338,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "graph_ms_per_step": round(graph_ms, 4) if graph_ms is not None else None,
         "higher_is_better": higher,
         "scaling": "weak",
         "vs_baseline": None,
