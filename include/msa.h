@@ -29,6 +29,10 @@
  *    device memory of at least the size the matching *_workspace_size returns.
  *  - bf16 arrays (and the scan's optional key norms, the prefill's output) are moved in
  *    16-byte vectors: their pointers must be 16-byte aligned, else MSA_ERR_SHAPE.
+ *  - An array with no elements may be NULL: the token rows of a memory with no tokens
+ *    (n_tok == 0), and every per-block array (pooled K/V, route keys, norms, block map)
+ *    of a memory with no blocks (n_blk == 0, e.g. every document empty).  Such a memory
+ *    scores -inf for every document.
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls
  *    validate on the host, enqueue kernels on `stream` and return; results are
  *    valid once the stream has been synchronised.  No call synchronises.

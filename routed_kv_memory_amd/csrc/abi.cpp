@@ -141,7 +141,9 @@ MSA_API int msa_pool_blocks(int32_t n_layers, const uint16_t* k, const uint16_t*
                             int64_t n_tok, const int64_t* doc_tok_off, const int64_t* doc_blk_off, int32_t n_docs,
                             int64_t n_blk, uint16_t* kbar, uint16_t* vbar, uint16_t* krbar_route,
                             float* krbar_norm, void* stream) {
-  if (!k || !v || !kr || !doc_tok_off || !doc_blk_off || !kbar || !vbar || !krbar_route)
+  // token rows may be NULL when there are no tokens, outputs when there are no blocks
+  if ((n_tok > 0 && (!k || !v || !kr)) || !doc_tok_off || !doc_blk_off ||
+      (n_blk > 0 && (!kbar || !vbar || !krbar_route)))
     return fail(MSA_ERR_NULL, "msa_pool_blocks: null pointer");
   if (!all_aligned16({k, v, kr, kbar, vbar, krbar_route}))
     return fail(MSA_ERR_SHAPE, "msa_pool_blocks: bf16 arrays must be 16-byte aligned");
@@ -156,7 +158,7 @@ MSA_API int msa_pool_blocks(int32_t n_layers, const uint16_t* k, const uint16_t*
 
 MSA_API int msa_pack_route_keys(int32_t n_layers, const uint16_t* krbar_rows, int64_t n_blk, uint16_t* krbar_route,
                                 float* krbar_norm, void* stream) {
-  if (!krbar_rows || !krbar_route) return fail(MSA_ERR_NULL, "msa_pack_route_keys: null pointer");
+  if (n_blk > 0 && (!krbar_rows || !krbar_route)) return fail(MSA_ERR_NULL, "msa_pack_route_keys: null pointer");
   if (!all_aligned16({krbar_rows, krbar_route}))
     return fail(MSA_ERR_SHAPE, "msa_pack_route_keys: bf16 arrays must be 16-byte aligned");
   if (n_layers < 1 || n_blk < 0) return fail(MSA_ERR_SHAPE, "msa_pack_route_keys: n_layers=%d n_blk=%lld", n_layers,
@@ -170,7 +172,7 @@ MSA_API int msa_pack_route_keys(int32_t n_layers, const uint16_t* krbar_rows, in
 
 MSA_API int msa_block_doc_map(const int64_t* doc_blk_off, int32_t n_docs, int64_t n_blk, int32_t* blk_doc,
                               void* stream) {
-  if (!doc_blk_off || !blk_doc) return fail(MSA_ERR_NULL, "msa_block_doc_map: null pointer");
+  if (!doc_blk_off || (n_blk > 0 && !blk_doc)) return fail(MSA_ERR_NULL, "msa_block_doc_map: null pointer");
   if (n_docs < 1 || n_blk < 0)
     return fail(MSA_ERR_SHAPE, "msa_block_doc_map: n_docs=%d n_blk=%lld", n_docs, (long long)n_blk);
   if (n_blk >= (int64_t)INT32_MAX - 32) return fail(MSA_ERR_UNSUPPORTED, "msa_block_doc_map: n_blk too large");
@@ -181,7 +183,7 @@ MSA_API int msa_block_doc_map(const int64_t* doc_blk_off, int32_t n_docs, int64_
 static int check_route_args(const char* fn, int32_t n_layers, const uint16_t* qr, int32_t B, int32_t T,
                             const uint16_t* krbar_route, const float* krbar_norm, int64_t n_blk,
                             const int32_t* blk_doc, int32_t n_docs) {
-  if (!qr || !krbar_route || !blk_doc) return fail(MSA_ERR_NULL, "%s: null pointer", fn);
+  if (!qr || (n_blk > 0 && (!krbar_route || !blk_doc))) return fail(MSA_ERR_NULL, "%s: null pointer", fn);
   if (!all_aligned16({qr, krbar_route, krbar_norm}))
     return fail(MSA_ERR_SHAPE, "%s: qr, the route keys and their norms must be 16-byte aligned", fn);
   if (n_layers < 1 || B < 1 || T < 1 || n_docs < 1 || n_blk < 0)
@@ -339,7 +341,7 @@ MSA_API int msa_gather_ctx(int32_t n_layers, int32_t B, const int32_t* topk_ids,
                            const int64_t* doc_blk_off, int32_t n_docs, int32_t max_doc_blocks, const uint16_t* kbar,
                            const uint16_t* vbar, int64_t n_blk, int32_t max_ctx, uint16_t* ctx_k, uint16_t* ctx_v,
                            int32_t* ctx_len, void* stream) {
-  if (!topk_ids || !doc_blk_off || !kbar || !vbar || !ctx_k || !ctx_v || !ctx_len)
+  if (!topk_ids || !doc_blk_off || (n_blk > 0 && (!kbar || !vbar)) || !ctx_k || !ctx_v || !ctx_len)
     return fail(MSA_ERR_NULL, "msa_gather_ctx: null pointer");
   if (!all_aligned16({kbar, vbar, ctx_k, ctx_v}))
     return fail(MSA_ERR_SHAPE, "msa_gather_ctx: bf16 arrays must be 16-byte aligned");

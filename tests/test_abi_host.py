@@ -153,3 +153,24 @@ def test_noalloc_route_topk_rejects_oversized_scratch_on_the_host(msa):
     assert lib.msa_route_topk_noalloc(1, None, 1, 64, fake, None, 1000, fake, 100, 16, fake, None, None, None) == 1
     assert lib.msa_route_topk_noalloc(1, fake, 1, 64, fake, None, 1000, fake, 10, 16, fake, None, None, None) == 2
     assert lib.msa_route_topk_noalloc(1, fake, 1, 64, fake, None, 1000, fake, 1000, 300, fake, None, None, None) == 3
+
+
+def test_empty_arrays_may_be_null(msa):
+    """A memory with no tokens and no blocks (every document empty) passes NULL for its empty
+    arrays; pooling, packing and the block map then have nothing to do and return before any
+    device call.  A NULL array that does have elements is still refused."""
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced
+    lib = msa.lib()
+    # n_tok = 0, n_blk = 0: token rows and every per-block output NULL
+    assert lib.msa_pool_blocks(2, None, None, None, 0, fake, fake, 5, 0, None, None, None, None, None) == 0
+    assert lib.msa_pack_route_keys(2, None, 0, None, None, None) == 0
+    assert lib.msa_block_doc_map(fake, 5, 0, None, None) == 0
+    # the same NULLs with elements present
+    assert lib.msa_pool_blocks(2, None, fake, fake, 10, fake, fake, 5, 1, fake, fake, fake, None, None) == 1
+    assert lib.msa_pool_blocks(2, fake, fake, fake, 10, fake, fake, 5, 1, None, fake, fake, None, None) == 1
+    assert lib.msa_pack_route_keys(2, None, 3, fake, None, None) == 1
+    assert lib.msa_block_doc_map(fake, 5, 3, None, None) == 1
+    assert lib.msa_route_scores(1, fake, 1, 8, None, None, 16, fake, 1, 0, fake, None) == 1
+    assert lib.msa_gather_ctx(1, 1, fake, 4, fake, 10, 8, None, fake, 100, 32, fake, fake, fake, None) == 1
+

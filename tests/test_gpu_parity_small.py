@@ -288,6 +288,61 @@ def test_pool_ragged_documents():
     assert np.all(untile_norms(krn, tiles * 16)[:, n_blk:] == 0)
 
 
+@pytest.mark.parametrize("T,B", [(8, 2), (64, 1), (130, 2)])
+def test_degenerate_memories(T, B):
+    """The memory's degenerate cases through the whole path: every document empty (no tokens, no
+    blocks: empty arrays passed as NULL, every score -inf, the top-k the first k ids, empty
+    contexts, decode and prefill over the local rows alone), and a single document with k = 1."""
+    print("case: degenerate memories T=%d B=%d" % (T, B), flush=True)
+    rng = np.random.default_rng(71 + T + B)
+    L, Hq, n_loc = 2, 32, 24
+    for lens, k in (([0, 0, 0, 0, 0], 3), ([100], 1)):
+        tok = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        n_tok = int(tok[-1])
+        blk, n_blk, max_db = msa.msa_block_offsets_host(torch.from_numpy(tok))
+        off = blk.numpy()
+        n_docs = len(lens)
+        kt, vt, rt = (rand_bf16(rng, (L, n_tok, 8, 128)) for _ in range(3))
+        tiles = msa.msa_route_tiles(n_blk)
+        kbar = torch.empty((L, n_blk, 8, 128), dtype=torch.bfloat16, device=DEV)
+        vbar = torch.empty_like(kbar)
+        krt = torch.empty((L, tiles * 16, 8, 128), dtype=torch.bfloat16, device=DEV)
+        krn = torch.empty((L, tiles * 16, 8), dtype=torch.float32, device=DEV)
+        blk_d = blk.to(DEV)
+        msa.msa_pool_blocks(to_dev_bf16(kt), to_dev_bf16(vt), to_dev_bf16(rt), torch.from_numpy(tok).to(DEV), blk_d,
+                            n_blk, kbar, vbar, krt, krn)
+        blk_doc = torch.empty(tiles * 16, dtype=torch.int32, device=DEV)
+        msa.msa_block_doc_map(blk_d, n_blk, blk_doc)
+        qr = rand_bf16(rng, (L, B, T, 8, 128))
+        ids, sc, dsc = route(to_dev_bf16(qr), krt, krn, n_blk, blk_d, k, blk_doc=blk_doc)
+        max_ctx = max(1, k * max_db)
+        ck, cv, cl = gather_all(ids, blk_d, max_db, kbar, vbar, max_ctx=max_ctx)
+        q = rand_bf16(rng, (L, B, Hq, 128))
+        lk, lv = rand_bf16(rng, (L, B, n_loc, 8, 128)), rand_bf16(rng, (L, B, n_loc, 8, 128))
+        ll = torch.full((L, B), n_loc, dtype=torch.int32, device=DEV)
+        out = decode_all(to_dev_bf16(q), ck, cv, cl, to_dev_bf16(lk), to_dev_bf16(lv), ll)
+        torch.cuda.synchronize()
+        if n_blk:
+            kb_o, vb_o, kr_o = (O.pool(x, tok, off) for x in (kt, vt, rt))
+            assert np.array_equal(u16(kbar), kb_o) and np.array_equal(u16(vbar), vb_o)
+            assert np.array_equal(untile_keys(krt, n_blk), kr_o)
+        else:
+            kb_o = vb_o = kr_o = np.zeros((L, 0, 8, 128), np.uint16)
+        for l in range(L):
+            kr_rows = kr_o[l]
+            for b in range(B):
+                S_o = O.doc_scores(qr[l, b], kr_rows, off)
+                d = dsc.cpu().numpy()[l, b]
+                fin = np.isfinite(S_o)
+                assert np.array_equal(fin, np.isfinite(d)) and np.all(d[~fin] == -np.inf)
+                assert np.max(np.abs(S_o[fin] - d[fin]), initial=0.0) < SCORE_TOL
+                assert_topk(ids.cpu().numpy()[l, b], sc.cpu().numpy()[l, b], d, S_o, k)
+                rk, rv = O.gather(ids.cpu().numpy()[l, b], off, kb_o[l], vb_o[l])
+                assert int(cl.cpu()[l, b]) == rk.shape[0] == (0 if not n_blk else n_blk)
+                ref = O.decode(q[l, b], rk, rv, lk[l, b], lv[l, b], SCALE)
+                assert_decode(out.cpu().numpy()[l, b], ref)
+
+
 # ------------------------------------------------------------------ gather / decode edges
 
 @pytest.mark.parametrize("Hq", [8, 16, 32, 64])
