@@ -938,7 +938,8 @@ def cpu_baseline(cfg, di, blk_off, seconds, unit, pool_args, scale):
     q, lk, lv, ll = di.decode_inputs()
     qr = di.qr()
     t_total, layers = 0.0, 0
-    for l in range(cfg.n_layers):
+    while True:                 # layers in turn (again from layer 0 when a memory has few of them)
+        l = layers % cfg.n_layers
         xs = [u16(a[l:l + 1]) for a in (kt, vt, krt_)]
         qr_l, q_l = u16(qr[l, 0]), u16(q[l, 0])
         nl = int(ll[l, 0])
@@ -953,8 +954,12 @@ def cpu_baseline(cfg, di, blk_off, seconds, unit, pool_args, scale):
         layers += 1
         if t_total + t_total / layers > seconds:
             break
-    work = ("whole path (pooling of K, V, Kr; scan; top-%d; gather; decode of query 0) of layer%s 0..%d, "
-            "%d tokens per layer" % (cfg.k, "" if layers == 1 else "s", layers - 1, n_tok))
+    if layers <= cfg.n_layers:
+        span = "layer%s 0..%d" % ("" if layers == 1 else "s", layers - 1)
+    else:
+        span = "%d layer passes over layer%s 0..%d" % (layers, "" if cfg.n_layers == 1 else "s", cfg.n_layers - 1)
+    work = ("whole path (pooling of K, V, Kr; scan; top-%d; gather; decode of query 0) of %s, "
+            "%d tokens per layer" % (cfg.k, span, n_tok))
     if unit == "ms":
         v = t_total * 1e3 / layers * cfg.n_layers
     else:
